@@ -1,0 +1,200 @@
+"""The oracle for paged decode attention and the paged cache write.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` import this package.  The product path
+(``paged_kv_cache_309_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``paged_oracle.c`` (plain C, IEEE double, compiled
+with gcc); this module only marshals NumPy arrays into it.  What the C code
+computes, and the passages of the pages it follows, is described at the top
+of that file.
+
+Pools handled here are flat NumPy arrays of the element storage type:
+``float32`` for fp32, ``float16`` for fp16, and ``uint16`` bit patterns for
+bfloat16.  Their layout is the C file's business; this wrapper never indexes
+into them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "paged_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libpaged_oracle.so")
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+_ERRORS = {
+    1: "bad argument",
+    2: "block-table entry outside the pool",
+    3: "context length beyond the block table",
+    4: "slot beyond the pool",
+    5: "two tokens write one slot",
+    6: "out of memory",
+}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile paged_oracle.c into libpaged_oracle.so with gcc."""
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                        "-pthread", "-Wall", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def _load(path: str | None = None):
+    global _lib
+    with _lib_lock:
+        if _lib is None or path is not None:
+            lib = ctypes.CDLL(path or build())
+            P = ctypes.c_void_p
+            lib.oracle_reshape_and_cache.restype = ctypes.c_int
+            lib.oracle_reshape_and_cache.argtypes = [
+                P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_paged_decode.restype = ctypes.c_int
+            lib.oracle_paged_decode.argtypes = [
+                P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_widen.restype = ctypes.c_int
+            lib.oracle_widen.argtypes = [P, P, ctypes.c_int64, ctypes.c_int]
+            if path is not None:
+                return lib
+            _lib = lib
+    return _lib
+
+
+class use_library:
+    """Context manager that points this module at another build of the
+    oracle (the tests use it to check that planted mistakes are caught)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _load()
+        lib = _load(self.path)
+        with _lib_lock:
+            _lib = lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        with _lib_lock:
+            _lib = self._saved
+        return False
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise OracleError(_ERRORS.get(rc, f"error {rc}"))
+
+
+def default_threads() -> int:
+    # at most 16: the share of host cores one GPU's job may use
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def new_pool(num_blocks: int, num_kv_heads: int, block_size: int,
+             head_dim: int, dtype: str, fill: str = "nan"):
+    """Two flat pools (K, V) of the element storage type, filled with NaN
+    bit patterns (``fill='nan'``) or zeros."""
+    n = num_blocks * num_kv_heads * block_size * head_dim
+    st = STORAGE[dtype]
+    if fill == "zero":
+        return np.zeros(n, st), np.zeros(n, st)
+    if dtype == "bf16":
+        pat = np.uint16(0x7FC1)
+    elif dtype == "f16":
+        pat = np.float16(np.nan)
+    else:
+        pat = np.float32(np.nan)
+    k = np.empty(n, st)
+    k.fill(pat)
+    return k, k.copy()
+
+
+def reshape_and_cache(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray,
+                      v_cache: np.ndarray, slot_mapping: np.ndarray,
+                      num_kv_heads: int, head_dim: int, block_size: int,
+                      num_blocks: int, dtype: str) -> None:
+    """Write token i's K/V ([T, Hkv, D]) into slot slot_mapping[i] of the
+    flat pools, in place."""
+    st = STORAGE[dtype]
+    k = np.ascontiguousarray(k, dtype=st)
+    v = np.ascontiguousarray(v, dtype=st)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k_cache.dtype == st and v_cache.dtype == st
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    n = num_blocks * num_kv_heads * block_size * head_dim
+    assert k_cache.size == n and v_cache.size == n
+    T = slots.shape[0]
+    assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    _check(_load().oracle_reshape_and_cache(
+        _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slots), T,
+        num_kv_heads, head_dim, block_size, num_blocks, DTYPES[dtype]))
+
+
+def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 block_tables: np.ndarray, context_lens: np.ndarray,
+                 scale: float, block_size: int, num_kv_heads: int,
+                 num_blocks: int, dtype: str, sel=None,
+                 threads: int | None = None) -> np.ndarray:
+    """Decode attention in float64.
+
+    q: [S, Hq, D] storage array.  Returns [S, Hq, D] float64, or, when
+    ``sel`` is an [N, 2] array of (seq, head) pairs, [N, D] float64.
+    """
+    st = STORAGE[dtype]
+    q = np.ascontiguousarray(q, dtype=st)
+    S, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert bt.ndim == 2 and bt.shape[0] == S and cl.shape == (S,)
+    if sel is None:
+        out = np.empty((S, Hq, D), np.float64)
+        sel_arr, nsel, sel_ptr = None, 0, None
+    else:
+        sel_arr = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+        nsel = sel_arr.shape[0]
+        out = np.empty((nsel, D), np.float64)
+        sel_ptr = _ptr(sel_arr)
+    _check(_load().oracle_paged_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+        float(scale), block_size, S, Hq, num_kv_heads, D, num_blocks,
+        bt.shape[1], DTYPES[dtype], sel_ptr, nsel,
+        threads or default_threads()))
+    return out
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """The oracle's own element decoding (storage -> float64)."""
+    a = np.ascontiguousarray(a, dtype=STORAGE[dtype])
+    out = np.empty(a.shape, np.float64)
+    _check(_load().oracle_widen(_ptr(a), _ptr(out), a.size, DTYPES[dtype]))
+    return out

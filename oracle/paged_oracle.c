@@ -1,0 +1,387 @@
+/*
+ * paged_oracle.c - the oracle for paged decode attention and for the
+ * cache write that fills the paged KV pool.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  The product path (the HIP library
+ * and its Python binding) never calls it, and it shares no code, header or
+ * constant with that path.
+ *
+ * What it computes, in IEEE double precision and in the plainest order:
+ *
+ *  1. The cache write.  A KV cache is cut into fixed-size blocks, and a
+ *     token's key and value live in one slot of one physical block
+ *     ("Why vLLM Uses PagedAttention", section "The insight": a page maps to
+ *     a KV block, a byte to one token's KV; section "The mechanism": 16-token
+ *     blocks by default).  A slot number is physical_block * block_size +
+ *     offset_in_block.  Each new token's K and V bits are copied into the
+ *     slot it is given; every other byte of the pool stays as it was.
+ *
+ *  2. Decode attention.  For every sequence s and query head h the result is
+ *     ordinary single-query attention softmax(q . K^T * scale) . V over the
+ *     sequence's first context_lens[s] tokens ("PagedAttention: how vLLM
+ *     manages the KV cache", section "PagedAttention changes addressing
+ *     inside attention": the computation is that of ordinary attention, only
+ *     the way K and V are located changes).  K and V of token t are reached
+ *     through the block table: logical block t / block_size, offset
+ *     t % block_size, physical block block_tables[s][t / block_size]
+ *     ("Paged Attention" placement notes, section "Paged Attention's
+ *     Approach": the worked request whose token 48 lands in logical block 3;
+ *     "Why vLLM Uses PagedAttention", section "The mechanism": the block table
+ *     maps logical to physical blocks like a page table).
+ *
+ *     The softmax is done in two passes (all logits, then their maximum,
+ *     then the weights), not with a running maximum, so that it shares no
+ *     algorithm with the device kernels.
+ *
+ * Readings of the pages (they are silent or garbled on these points):
+ *   - the context length counts the token being decoded, which was written
+ *     to the cache just before attention, so tokens 0 .. L-1 are attended
+ *     (the worked example attends to tokens 0-48 while token 48 is placed);
+ *   - the number of blocks walked is ceil(L / block_size): a partly filled
+ *     last block is still read, only up to token L-1;
+ *   - K and V are two pools of the same block structure (the sketch keeps
+ *     them in one tensor);
+ *   - grouped-query attention maps query head h to KV head
+ *     h / (num_heads / num_kv_heads) (consecutive groups);
+ *   - L = 0 yields an all-zero output;
+ *   - a negative slot means "no write" (a padding token); a slot beyond the
+ *     pool, or two writes to one slot, is rejected with an error code.
+ *
+ * Pool layouts (the product library documents the same two formulas; they
+ * are restated here independently):
+ *   K element (block p, kv head g, offset o, dim d):
+ *       ((p * Hkv + g) * bs + o) * D + d
+ *   V element (block p, kv head g, offset o, dim d):
+ *       (p * Hkv + g) * bs * D + (o / 4) * 4 * D + d * 4 + (o % 4)
+ *   i.e. V keeps each run of four consecutive tokens of one dimension next to
+ *   each other.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+enum {
+  OR_OK = 0,
+  OR_ERR_ARG = 1,        /* bad sizes or dtype */
+  OR_ERR_TABLE = 2,      /* a block-table entry outside [0, num_blocks) */
+  OR_ERR_CONTEXT = 3,    /* context length above max_blocks * block_size */
+  OR_ERR_SLOT_RANGE = 4, /* slot >= num_blocks * block_size */
+  OR_ERR_SLOT_DUP = 5,   /* two tokens share one slot */
+  OR_ERR_NOMEM = 6
+};
+
+/* ---- element decoding ------------------------------------------------ */
+
+/* IEEE binary16 -> double, written out from the format's definition:
+ * sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double half_bits_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1f;
+  int fr = h & 0x3ff;
+  double v;
+  if (ex == 0) {
+    v = ldexp((double)fr, -24); /* subnormal: fr * 2^-14 * 2^-10 */
+  } else if (ex == 31) {
+    v = fr ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + fr), ex - 25); /* (1 + fr/1024) * 2^(ex-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16 -> double: a bfloat16 is the upper half of a binary32. */
+static double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void *base, size_t idx, int dtype) {
+  switch (dtype) {
+  case OR_F32:
+    return (double)((const float *)base)[idx];
+  case OR_F16:
+    return half_bits_to_double(((const uint16_t *)base)[idx]);
+  default:
+    return bf16_bits_to_double(((const uint16_t *)base)[idx]);
+  }
+}
+
+static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : 2; }
+
+/* ---- pool addressing ---------------------------------------------------- */
+
+static size_t k_index(size_t p, size_t g, size_t o, size_t d, size_t hkv,
+                      size_t bs, size_t hd) {
+  return ((p * hkv + g) * bs + o) * hd + d;
+}
+
+static size_t v_index(size_t p, size_t g, size_t o, size_t d, size_t hkv,
+                      size_t bs, size_t hd) {
+  return (p * hkv + g) * bs * hd + (o / 4) * 4 * hd + d * 4 + (o % 4);
+}
+
+/* ---- the cache write ----------------------------------------------------- */
+
+/* k, v: [num_tokens, num_kv_heads, head_dim] in the pool's element type.
+ * k_cache, v_cache: flat pools of num_blocks * num_kv_heads * block_size *
+ * head_dim elements.  Returns an OR_* code; on error the pools are left
+ * untouched. */
+int oracle_reshape_and_cache(const void *k, const void *v, void *k_cache,
+                             void *v_cache, const int64_t *slot_mapping,
+                             int64_t num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int64_t num_blocks,
+                             int dtype) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 || num_blocks < 0 || dtype < OR_F32 ||
+      dtype > OR_BF16)
+    return OR_ERR_ARG;
+  const int64_t nslots = num_blocks * (int64_t)block_size;
+  /* precheck: every slot in range, no slot written twice */
+  unsigned char *seen = calloc((size_t)(nslots / 8 + 1), 1);
+  if (!seen)
+    return OR_ERR_NOMEM;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t s = slot_mapping[i];
+    if (s < 0)
+      continue;
+    if (s >= nslots) {
+      free(seen);
+      return OR_ERR_SLOT_RANGE;
+    }
+    if (seen[s / 8] & (1u << (s % 8))) {
+      free(seen);
+      return OR_ERR_SLOT_DUP;
+    }
+    seen[s / 8] |= (unsigned char)(1u << (s % 8));
+  }
+  free(seen);
+
+  const size_t eb = (size_t)elem_bytes(dtype);
+  const size_t hkv = (size_t)num_kv_heads, hd = (size_t)head_dim,
+               bs = (size_t)block_size;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t s = slot_mapping[i];
+    if (s < 0)
+      continue;
+    size_t p = (size_t)(s / block_size), o = (size_t)(s % block_size);
+    for (size_t g = 0; g < hkv; ++g) {
+      for (size_t d = 0; d < hd; ++d) {
+        size_t src = ((size_t)i * hkv + g) * hd + d;
+        memcpy((char *)k_cache + k_index(p, g, o, d, hkv, bs, hd) * eb,
+               (const char *)k + src * eb, eb);
+        memcpy((char *)v_cache + v_index(p, g, o, d, hkv, bs, hd) * eb,
+               (const char *)v + src * eb, eb);
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* ---- decode attention ------------------------------------------------------ */
+
+struct decode_job {
+  double *out;
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_tables, *context_lens;
+  double scale;
+  int block_size, num_seqs, num_heads, num_kv_heads, head_dim;
+  int64_t num_blocks;
+  int max_blocks_per_seq, dtype;
+  const int32_t *sel; /* optional (seq, head) pairs */
+  int64_t num_items;
+  int num_threads;
+  int status; /* first error seen (written under the lock) */
+  pthread_mutex_t lock;
+};
+
+/* One (sequence, query head): fills out[0 .. head_dim-1]. */
+static int decode_one(const struct decode_job *jb, int s, int h, double *out) {
+  const int hd = jb->head_dim, bs = jb->block_size;
+  const int group = jb->num_heads / jb->num_kv_heads;
+  const int g = h / group;
+  const int L = jb->context_lens[s];
+  for (int d = 0; d < hd; ++d)
+    out[d] = 0.0;
+  if (L <= 0)
+    return OR_OK;
+  if ((int64_t)L > (int64_t)jb->max_blocks_per_seq * bs)
+    return OR_ERR_CONTEXT;
+
+  const size_t hkv = (size_t)jb->num_kv_heads;
+  const size_t qbase = ((size_t)s * jb->num_heads + h) * hd;
+  const int32_t *table = jb->block_tables + (size_t)s * jb->max_blocks_per_seq;
+
+  double *x = malloc(sizeof(double) * (size_t)L);
+  if (!x)
+    return OR_ERR_NOMEM;
+
+  /* pass 1: logits x_t = scale * sum_d q[d] * K_t[d] */
+  for (int t = 0; t < L; ++t) {
+    int p = table[t / bs];
+    int o = t % bs;
+    if (p < 0 || p >= jb->num_blocks) {
+      free(x);
+      return OR_ERR_TABLE;
+    }
+    double dot = 0.0;
+    for (int d = 0; d < hd; ++d)
+      dot += load_elem(jb->q, qbase + d, jb->dtype) *
+             load_elem(jb->k_cache,
+                       k_index((size_t)p, (size_t)g, (size_t)o, (size_t)d, hkv,
+                               (size_t)bs, (size_t)hd),
+                       jb->dtype);
+    x[t] = jb->scale * dot;
+  }
+
+  /* the maximum logit */
+  double m = x[0];
+  for (int t = 1; t < L; ++t)
+    if (x[t] > m)
+      m = x[t];
+
+  /* pass 2: weights w_t = exp(x_t - m), their sum, and sum_t w_t * V_t */
+  double z = 0.0;
+  for (int t = 0; t < L; ++t) {
+    int p = table[t / bs];
+    int o = t % bs;
+    double w = exp(x[t] - m);
+    z += w;
+    for (int d = 0; d < hd; ++d)
+      out[d] += w * load_elem(jb->v_cache,
+                              v_index((size_t)p, (size_t)g, (size_t)o,
+                                      (size_t)d, hkv, (size_t)bs, (size_t)hd),
+                              jb->dtype);
+  }
+  for (int d = 0; d < hd; ++d)
+    out[d] /= z;
+  free(x);
+  return OR_OK;
+}
+
+struct worker_arg {
+  struct decode_job *jb;
+  int tid;
+};
+
+static void *decode_worker(void *argp) {
+  struct worker_arg *wa = argp;
+  struct decode_job *jb = wa->jb;
+  for (int64_t it = wa->tid; it < jb->num_items; it += jb->num_threads) {
+    int s, h;
+    if (jb->sel) {
+      s = jb->sel[2 * it];
+      h = jb->sel[2 * it + 1];
+    } else {
+      s = (int)(it / jb->num_heads);
+      h = (int)(it % jb->num_heads);
+    }
+    int rc = decode_one(jb, s, h, jb->out + (size_t)it * jb->head_dim);
+    if (rc != OR_OK) {
+      pthread_mutex_lock(&jb->lock);
+      if (jb->status == OR_OK)
+        jb->status = rc;
+      pthread_mutex_unlock(&jb->lock);
+      return NULL;
+    }
+  }
+  return NULL;
+}
+
+/* out: double [num_items, head_dim].  Without `sel`, the items are every
+ * (s, h) in row-major order (num_items = num_seqs * num_heads) and `out` is
+ * [num_seqs, num_heads, head_dim]; with `sel` (num_sel pairs of int32
+ * (seq, head)), item i is pair i.  q: [num_seqs, num_heads, head_dim];
+ * block_tables: [num_seqs, max_blocks_per_seq]; context_lens: [num_seqs].
+ * The items are spread over `num_threads` POSIX threads; every item is
+ * computed on its own, so the result does not depend on the thread count. */
+int oracle_paged_decode(double *out, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, float scale,
+                        int block_size, int num_seqs, int num_heads,
+                        int num_kv_heads, int head_dim, int64_t num_blocks,
+                        int max_blocks_per_seq, int dtype, const int32_t *sel,
+                        int64_t num_sel, int num_threads) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
+      dtype < OR_F32 || dtype > OR_BF16 || num_threads <= 0)
+    return OR_ERR_ARG;
+  struct decode_job jb;
+  memset(&jb, 0, sizeof jb);
+  jb.out = out;
+  jb.q = q;
+  jb.k_cache = k_cache;
+  jb.v_cache = v_cache;
+  jb.block_tables = block_tables;
+  jb.context_lens = context_lens;
+  jb.scale = (double)scale; /* the float argument, exactly */
+  jb.block_size = block_size;
+  jb.num_seqs = num_seqs;
+  jb.num_heads = num_heads;
+  jb.num_kv_heads = num_kv_heads;
+  jb.head_dim = head_dim;
+  jb.num_blocks = num_blocks;
+  jb.max_blocks_per_seq = max_blocks_per_seq;
+  jb.dtype = dtype;
+  jb.sel = sel;
+  jb.num_items = sel ? num_sel : (int64_t)num_seqs * num_heads;
+  if (sel) {
+    for (int64_t i = 0; i < num_sel; ++i)
+      if (sel[2 * i] < 0 || sel[2 * i] >= num_seqs || sel[2 * i + 1] < 0 ||
+          sel[2 * i + 1] >= num_heads)
+        return OR_ERR_ARG;
+  }
+  jb.num_threads = num_threads;
+  jb.status = OR_OK;
+  pthread_mutex_init(&jb.lock, NULL);
+
+  pthread_t *th = malloc(sizeof(pthread_t) * (size_t)num_threads);
+  struct worker_arg *wa = malloc(sizeof(struct worker_arg) * (size_t)num_threads);
+  if (!th || !wa) {
+    free(th);
+    free(wa);
+    pthread_mutex_destroy(&jb.lock);
+    return OR_ERR_NOMEM;
+  }
+  int started = 0;
+  for (int t = 0; t < num_threads; ++t) {
+    wa[t].jb = &jb;
+    wa[t].tid = t;
+    if (pthread_create(&th[t], NULL, decode_worker, &wa[t]) != 0)
+      break;
+    ++started;
+  }
+  if (started == 0) { /* no thread could start: run the items here */
+    wa[0].jb = &jb;
+    wa[0].tid = 0;
+    jb.num_threads = 1;
+    decode_worker(&wa[0]);
+  } else if (started < num_threads) {
+    /* items owned by threads that never started: run them here */
+    for (int t = started; t < num_threads; ++t)
+      decode_worker(&wa[t]);
+  }
+  for (int t = 0; t < started; ++t)
+    pthread_join(th[t], NULL);
+  free(th);
+  free(wa);
+  pthread_mutex_destroy(&jb.lock);
+  return jb.status;
+}
+
+/* Widen n stored elements to double with the decoders above; exported so
+ * the decoders themselves can be checked against a library conversion. */
+int oracle_widen(const void *src, double *dst, int64_t n, int dtype) {
+  if (n < 0 || dtype < OR_F32 || dtype > OR_BF16)
+    return OR_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    dst[i] = load_elem(src, (size_t)i, dtype);
+  return OR_OK;
+}
