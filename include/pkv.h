@@ -1,0 +1,206 @@
+/*
+ * pkv.h - paged decode attention for AMD MI355X (gfx950): the C ABI.
+ *
+ * A KV cache is cut into fixed-size blocks of `block_size` tokens that may
+ * sit anywhere in a pool; each sequence owns a block table that maps its
+ * logical blocks (tokens 0..15, 16..31, ...) to physical blocks of the pool,
+ * like a page table ("Why vLLM Uses PagedAttention", sections "The insight"
+ * and "The mechanism").  This library provides the device side of one
+ * decode step over such a cache:
+ *
+ *   reshape_and_cache             writes every new token's K and V into the
+ *                                 slot it was given;
+ *   paged_attention_decode        single-query attention for every
+ *                                 (sequence, query head), walking the block
+ *                                 table, in one kernel launch;
+ *   paged_attention_decode_split  the same result for long contexts: the
+ *                                 context is cut into partitions that are
+ *                                 processed independently, then a second
+ *                                 kernel merges the partial results.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All data pointers are DEVICE pointers (HBM), owned by the caller.  The
+ *   library allocates nothing, keeps no mutable state and may be called from
+ *   several host threads.
+ * - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *   NULL means the default stream) and the call returns before it runs.
+ * - One element type covers q, out, k, v and both caches (pkv_dims.dtype).
+ * - Every base pointer must be 16-byte aligned.
+ * - Return value: PKV_OK (0) or a positive pkv_status.  On an error nothing
+ *   is enqueued.  The library never aborts and never prints.  Only values
+ *   the host can see are validated; device-resident indices are
+ *   preconditions (see each call), and a kernel never reads or writes
+ *   outside the buffers described here whatever those indices hold.
+ *
+ * Memory layouts (row-major, contiguous; Hq = num_heads, Hkv = num_kv_heads,
+ * D = head_dim, bs = block_size, NB = num_blocks, S = num_seqs)
+ * ---------------------------------------------------------------------------
+ *   q, out        [S, Hq, D]
+ *   k, v          [num_tokens, Hkv, D]            (reshape_and_cache input)
+ *   k_cache       [NB, Hkv, bs, D]
+ *                 element (p, g, o, d) at ((p*Hkv + g)*bs + o)*D + d
+ *   v_cache       [NB, Hkv, bs/4, D, 4]
+ *                 element (p, g, o, d) at
+ *                 (p*Hkv + g)*bs*D + (o/4)*4*D + d*4 + o%4
+ *                 (runs of four consecutive tokens of one dimension are
+ *                 adjacent, so that the token axis - the contraction axis of
+ *                 the probability-times-value product - is contiguous)
+ *   block_tables  int32 [S, max_blocks_per_seq]; entry j of row s is the
+ *                 physical block holding tokens j*bs .. j*bs+bs-1
+ *   context_lens  int32 [S]
+ *   slot_mapping  int64 [num_tokens]; slot = physical_block*bs + offset
+ *
+ * Query head h reads KV head h / (Hq / Hkv) (consecutive groups).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compatible with hipStream_t (which is `struct ihipStream_t *`). */
+typedef struct ihipStream_t *pkv_stream_t;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,  /* IEEE binary32 */
+  PKV_F16 = 1,  /* IEEE binary16 */
+  PKV_BF16 = 2  /* bfloat16 */
+} pkv_dtype;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  PKV_ERR_DTYPE = 2,       /* dtype not one of pkv_dtype */
+  PKV_ERR_BLOCK_SIZE = 3,  /* block_size not 16 or 32 */
+  PKV_ERR_HEAD_DIM = 4,    /* head_dim not 64 or 128 */
+  PKV_ERR_HEADS = 5,       /* heads <= 0, or num_heads % num_kv_heads != 0 */
+  PKV_ERR_SHAPE = 6,       /* a negative size, or a size too large to index */
+  PKV_ERR_ALIGN = 7,       /* a base pointer not 16-byte aligned */
+  PKV_ERR_PARTITION = 8,   /* partition_size not a positive multiple of
+                              block_size */
+  PKV_ERR_WORKSPACE = 9,   /* workspace NULL or smaller than required */
+  PKV_ERR_LAUNCH = 10,     /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_ALIAS = 11       /* out overlaps an input */
+} pkv_status;
+
+/* Sizes of one call.  Fields a call does not use are ignored. */
+typedef struct pkv_dims {
+  int32_t num_seqs;           /* S */
+  int32_t num_heads;          /* Hq, query heads */
+  int32_t num_kv_heads;       /* Hkv, key/value heads */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t num_blocks;         /* NB, blocks in the pool */
+  int32_t max_blocks_per_seq; /* row length of block_tables */
+  int32_t dtype;              /* a pkv_dtype */
+} pkv_dims;
+
+/*
+ * reshape_and_cache - write new tokens' keys and values into the cache.
+ *
+ * For every token i with slot = slot_mapping[i] >= 0: p = slot / block_size,
+ * o = slot % block_size, and for every KV head g the vectors k[i, g, :] and
+ * v[i, g, :] are copied bit for bit to k_cache[p, g, o, :] and
+ * v_cache[p, g, o, :].  Nothing else in the pools changes.  The write goes
+ * into the block a sequence is currently filling, or into a freshly
+ * allocated block when the last one is full ("Inside vLLM: How PagedAttention
+ * Eliminates KV-Cache Memory Waste", section "How It Works During
+ * Generation"; "PagedAttention: how vLLM manages the KV cache", section
+ * "Walk one request through the allocator"); the attention kernels read the
+ * cache through the same block tables ("PagedAttention - Virtual Memory for
+ * the KV Cache" explainer, chapter "vLLM - The Engine": attention and copy
+ * kernels traverse block tables).
+ *
+ * Uses dims->num_kv_heads, head_dim, num_blocks, dtype.
+ * Preconditions (device data, not checked): the non-negative slots are
+ * pairwise distinct.  A negative slot writes nothing (a padding token); a
+ * slot >= num_blocks*block_size writes nothing.
+ * k_cache and v_cache must not overlap k or v.
+ */
+int reshape_and_cache(const void *k, const void *v, void *k_cache,
+                      void *v_cache, const int64_t *slot_mapping,
+                      int num_tokens, int block_size, const pkv_dims *dims,
+                      pkv_stream_t stream);
+
+/*
+ * paged_attention_decode - single-query attention over a paged KV cache.
+ *
+ * For every sequence s and query head h, with L = context_lens[s] and
+ * g = h / (Hq/Hkv):
+ *     out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K_t) * V_t,
+ * over tokens t = 0 .. L-1, where K_t and V_t are read from physical block
+ * block_tables[s][t / block_size] at offset t % block_size.  This is the
+ * computation of ordinary attention; only the addressing goes through the
+ * block table ("PagedAttention: how vLLM manages the KV cache", section
+ * "PagedAttention changes addressing inside attention"; "Paged Attention"
+ * placement notes, section "Paged Attention's Approach": the kernel reads
+ * the table and walks the blocks of a request).  L counts the token being
+ * decoded, whose K/V were written by reshape_and_cache before this call.
+ * L = 0 gives an all-zero output row.
+ *
+ * Arithmetic: products and sums in fp32 whatever the storage type; the
+ * result is rounded to nearest-even into the storage type.  The result is
+ * deterministic and depends only on the logical contents, not on which
+ * physical blocks hold them.
+ *
+ * Preconditions (device data, not checked): 0 <= L <= max_blocks_per_seq *
+ * block_size (larger L is treated as that bound), and
+ * 0 <= block_tables[s][j] < num_blocks for j < ceil(L / block_size) (an
+ * entry outside the pool is read as block 0).  Table entries past
+ * ceil(L / block_size), and slots past L-1 in the last block, are never read.
+ * `out` must not overlap any input.
+ */
+int paged_attention_decode(void *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, float scale,
+                           int block_size, const pkv_dims *dims,
+                           pkv_stream_t stream);
+
+/*
+ * paged_attention_split_workspace_bytes - size of the fp32 workspace
+ * paged_attention_decode_split needs for these sizes.  Writes it to *bytes.
+ */
+int paged_attention_split_workspace_bytes(const pkv_dims *dims, int block_size,
+                                          int partition_size, size_t *bytes);
+
+/*
+ * paged_attention_decode_split - the same result as paged_attention_decode,
+ * computed in two launches for long contexts.
+ *
+ * Launch 1 cuts every sequence's context into partitions of partition_size
+ * tokens and, for every (sequence, head, partition), writes to `workspace`
+ * the partition's maximum logit, its sum of exponentials and its
+ * un-normalised weighted sum of values (fp32).  Launch 2 merges the
+ * partitions of each (sequence, head) by rescaling every partial to the
+ * largest maximum, and writes `out`.  The merge is an exact re-association
+ * of the softmax sum, so the two entry points agree up to rounding.
+ *
+ * partition_size: a positive multiple of block_size (512 is the usual
+ * choice).  workspace: device memory of at least the size returned by
+ * paged_attention_split_workspace_bytes; its contents on entry do not
+ * matter, and after the call it holds scratch data.  Arguments and
+ * preconditions are otherwise those of paged_attention_decode.
+ */
+int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
+                                 const void *v_cache,
+                                 const int32_t *block_tables,
+                                 const int32_t *context_lens, float scale,
+                                 int block_size, int partition_size,
+                                 void *workspace, size_t workspace_bytes,
+                                 const pkv_dims *dims, pkv_stream_t stream);
+
+/* A static, human-readable description of a status code. */
+const char *pkv_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,135 @@
+"""Paged decode attention for AMD MI355X (gfx950).
+
+Python binding of libpkv.so.  The functions below take torch tensors that
+live on the GPU, turn them into raw pointers, sizes and the current HIP
+stream, and call the C ABI (include/pkv.h).  They do no arithmetic: every
+step runs in the HIP kernels, and an error status raises PkvError.
+
+Cache tensors (allocate them with new_kv_cache):
+    k_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+    v_cache  [num_blocks, num_kv_heads, block_size // 4, head_dim, 4]
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PkvDims, PkvError
+
+__all__ = ["reshape_and_cache", "paged_attention_decode",
+           "paged_attention_decode_split", "split_workspace_bytes",
+           "new_kv_cache", "PkvError", "version"]
+
+_DTYPES = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
+           torch.bfloat16: _lib.PKV_BF16}
+
+
+def version() -> int:
+    return _lib.lib().pkv_version()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> int:
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpkv must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int,
+                 head_dim: int, dtype: torch.dtype, device="cuda",
+                 fill: float | None = None):
+    """Allocate (k_cache, v_cache) in the library's block layouts."""
+    k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim),
+                    dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, block_size // 4, head_dim, 4),
+                    dtype=dtype, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def _dims(q: torch.Tensor, k_cache: torch.Tensor,
+          block_tables: torch.Tensor) -> PkvDims:
+    S, Hq, D = q.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    return PkvDims(S, Hq, Hkv, D, NB, block_tables.shape[1], _dtype(q))
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write k[i], v[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64)."""
+    T, Hkv, D = k.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[2]
+    dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k))
+    _lib.check(_lib.lib().reshape_and_cache(
+        _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        T, bs, ctypes.byref(dims), _stream(stream)))
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor,
+                           k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float,
+                           block_size: int | None = None,
+                           stream=None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] . K) V over context_lens[s]
+    tokens reached through block_tables[s]; single launch."""
+    bs = block_size or k_cache.shape[2]
+    dims = _dims(q, k_cache, block_tables)
+    _lib.check(_lib.lib().paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), bs, ctypes.byref(dims),
+        _stream(stream)))
+    return out
+
+
+def split_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor,
+                          block_tables: torch.Tensor, partition_size: int,
+                          block_size: int | None = None) -> int:
+    bs = block_size or k_cache.shape[2]
+    dims = _dims(q, k_cache, block_tables)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.lib().paged_attention_split_workspace_bytes(
+        ctypes.byref(dims), bs, partition_size, ctypes.byref(n)))
+    return n.value
+
+
+def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 block_tables: torch.Tensor,
+                                 context_lens: torch.Tensor, scale: float,
+                                 partition_size: int,
+                                 workspace: torch.Tensor,
+                                 block_size: int | None = None,
+                                 stream=None) -> torch.Tensor:
+    """Same result as paged_attention_decode, in two launches: per-partition
+    partials into `workspace` (a device byte tensor of at least
+    split_workspace_bytes(...)), then the partition reduce."""
+    bs = block_size or k_cache.shape[2]
+    dims = _dims(q, k_cache, block_tables)
+    _lib.check(_lib.lib().paged_attention_decode_split(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), bs, int(partition_size),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(dims), _stream(stream)))
+    return out
+
+
+# load (and fail loudly) at import
+_lib.lib()

@@ -1,0 +1,256 @@
+// abi.hip - the exported C ABI: argument validation, kernel choice and
+// launch.  Every check runs before the first HIP call, so a rejected call
+// touches no device.
+#include <limits.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using u128 = unsigned __int128;
+
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checks shared by the decode entry points; fills the byte sizes.
+int check_decode(const pkv_dims *d, int block_size, size_t *q_bytes,
+                 size_t *cache_bytes) {
+  if (!d) return PKV_ERR_NULL;
+  if (d->dtype < PKV_F32 || d->dtype > PKV_BF16) return PKV_ERR_DTYPE;
+  if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_HEAD_DIM;
+  if (d->num_heads <= 0 || d->num_kv_heads <= 0 || d->num_heads % d->num_kv_heads != 0)
+    return PKV_ERR_HEADS;
+  if (d->num_seqs < 0 || d->num_blocks < 0 || d->max_blocks_per_seq < 0)
+    return PKV_ERR_SHAPE;
+  if (d->num_seqs > kMaxGridYZ) return PKV_ERR_SHAPE;
+  if ((int64_t)d->max_blocks_per_seq * block_size > INT_MAX / 2) return PKV_ERR_SHAPE;
+  const u128 e = (u128)elem_bytes(d->dtype);
+  const u128 qb = (u128)d->num_seqs * (u128)d->num_heads * (u128)d->head_dim * e;
+  const u128 cb = (u128)d->num_blocks * (u128)d->num_kv_heads * (u128)block_size *
+                  (u128)d->head_dim * e;
+  if (qb > ((u128)1 << 62) || cb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  *q_bytes = (size_t)qb;
+  *cache_bytes = (size_t)cb;
+  return PKV_OK;
+}
+
+int check_decode_ptrs(void *out, const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, const pkv_dims *d,
+                      size_t q_bytes, size_t cache_bytes) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  const size_t tb = (size_t)d->num_seqs * (size_t)d->max_blocks_per_seq * 4;
+  const size_t lb = (size_t)d->num_seqs * 4;
+  if (overlap(out, q_bytes, q, q_bytes) || overlap(out, q_bytes, k_cache, cache_bytes) ||
+      overlap(out, q_bytes, v_cache, cache_bytes) || overlap(out, q_bytes, block_tables, tb) ||
+      overlap(out, q_bytes, context_lens, lb))
+    return PKV_ERR_ALIAS;
+  return PKV_OK;
+}
+
+pkv::DecodeArgs make_args(void *out, const void *q, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, float scale,
+                          int block_size, const pkv_dims *d) {
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  // the softmax runs in base 2: exp(x * scale) = 2^(x * scale * log2 e)
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.num_seqs = d->num_seqs;
+  a.num_heads = d->num_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.num_blocks = d->num_blocks;
+  // an empty pool holds no token: every context is then treated as empty,
+  // so no block (not even the clamped block 0) is ever read
+  a.max_blocks = d->num_blocks > 0 ? d->max_blocks_per_seq : 0;
+  a.block_size = block_size;
+  a.part_tokens = 0;
+  a.num_parts = 1;
+  return a;
+}
+
+// Matrix cores when a KV head serves 2..16 query heads in fp16/bf16; the
+// vector kernel otherwise.
+bool use_mfma(const pkv_dims *d) {
+  const int G = d->num_heads / d->num_kv_heads;
+  return d->dtype != PKV_F32 && G >= 2 && G <= 16;
+}
+
+int num_partitions(const pkv_dims *d, int block_size, int partition_size) {
+  const int64_t ctx = (int64_t)d->max_blocks_per_seq * block_size;
+  return (int)((ctx + partition_size - 1) / partition_size);
+}
+
+int split_ws_bytes(const pkv_dims *d, int block_size, int partition_size,
+                   size_t *bytes) {
+  if (partition_size <= 0 || partition_size % block_size != 0) return PKV_ERR_PARTITION;
+  const int P = num_partitions(d, block_size, partition_size);
+  if (P > kMaxGridYZ) return PKV_ERR_PARTITION;
+  const u128 n = (u128)d->num_seqs * (u128)d->num_heads * (u128)(P > 0 ? P : 1);
+  const u128 b = n * (u128)(d->head_dim + 2) * 4;
+  if (b > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  *bytes = (size_t)b;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int reshape_and_cache(const void *k, const void *v, void *k_cache,
+                      void *v_cache, const int64_t *slot_mapping,
+                      int num_tokens, int block_size, const pkv_dims *dims,
+                      pkv_stream_t stream) {
+  if (!dims) return PKV_ERR_NULL;
+  if (dims->dtype < PKV_F32 || dims->dtype > PKV_BF16) return PKV_ERR_DTYPE;
+  if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
+  if (dims->head_dim != 64 && dims->head_dim != 128) return PKV_ERR_HEAD_DIM;
+  if (dims->num_kv_heads <= 0) return PKV_ERR_HEADS;
+  if (num_tokens < 0 || dims->num_blocks < 0) return PKV_ERR_SHAPE;
+  const u128 e = (u128)elem_bytes(dims->dtype);
+  const u128 tb = (u128)num_tokens * (u128)dims->num_kv_heads * (u128)dims->head_dim * e;
+  const u128 cb = (u128)dims->num_blocks * (u128)dims->num_kv_heads * (u128)block_size *
+                  (u128)dims->head_dim * e;
+  if (tb > ((u128)1 << 62) || cb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  if (overlap(k_cache, (size_t)cb, k, (size_t)tb) || overlap(k_cache, (size_t)cb, v, (size_t)tb) ||
+      overlap(v_cache, (size_t)cb, k, (size_t)tb) || overlap(v_cache, (size_t)cb, v, (size_t)tb) ||
+      overlap(k_cache, (size_t)cb, v_cache, (size_t)cb))
+    return PKV_ERR_ALIAS;
+  pkv::CacheWriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.num_blocks = dims->num_blocks;
+  const hipError_t err = pkv::launch_reshape_and_cache(
+      a, dims->dtype, dims->head_dim, block_size, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_decode(void *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, float scale,
+                           int block_size, const pkv_dims *dims,
+                           pkv_stream_t stream) {
+  size_t qb = 0, cb = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  const pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
+                                      context_lens, scale, block_size, dims);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t err =
+      use_mfma(dims)
+          ? pkv::launch_decode_mfma(a, dims->dtype, dims->head_dim, block_size, false, st)
+          : pkv::launch_decode_vector(a, dims->dtype, dims->head_dim, block_size, false, st);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_split_workspace_bytes(const pkv_dims *dims, int block_size,
+                                          int partition_size, size_t *bytes) {
+  if (!bytes) return PKV_ERR_NULL;
+  size_t qb = 0, cb = 0;
+  const int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  return split_ws_bytes(dims, block_size, partition_size, bytes);
+}
+
+int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
+                                 const void *v_cache,
+                                 const int32_t *block_tables,
+                                 const int32_t *context_lens, float scale,
+                                 int block_size, int partition_size,
+                                 void *workspace, size_t workspace_bytes,
+                                 const pkv_dims *dims, pkv_stream_t stream) {
+  size_t qb = 0, cb = 0, need = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  rc = split_ws_bytes(dims, block_size, partition_size, &need);
+  if (rc != PKV_OK) return rc;
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb) ||
+      overlap(workspace, need, k_cache, cb) || overlap(workspace, need, v_cache, cb))
+    return PKV_ERR_ALIAS;
+
+  pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
+                                context_lens, scale, block_size, dims);
+  const int P = num_partitions(dims, block_size, partition_size);
+  if (P == 0) {  // no token can be attended: the reduce writes zeros
+    a.num_parts = 1;
+  } else {
+    a.num_parts = P;
+  }
+  a.part_tokens = partition_size;
+  const size_t n = (size_t)dims->num_seqs * dims->num_heads * a.num_parts;
+  a.ws_o = static_cast<float *>(workspace);
+  a.ws_m = a.ws_o + n * dims->head_dim;
+  a.ws_l = a.ws_m + n;
+
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (P > 0) {
+    err = use_mfma(dims)
+              ? pkv::launch_decode_mfma(a, dims->dtype, dims->head_dim, block_size, true, st)
+              : pkv::launch_decode_vector(a, dims->dtype, dims->head_dim, block_size, true, st);
+  }
+  if (err == hipSuccess) err = pkv::launch_partition_reduce(a, dims->dtype, dims->head_dim, st);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_DTYPE: return "unsupported dtype";
+    case PKV_ERR_BLOCK_SIZE: return "block_size must be 16 or 32";
+    case PKV_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case PKV_ERR_HEADS: return "num_heads must be a positive multiple of num_kv_heads";
+    case PKV_ERR_SHAPE: return "a size is negative or too large";
+    case PKV_ERR_ALIGN: return "a pointer is not aligned (16 bytes for data)";
+    case PKV_ERR_PARTITION: return "partition_size must be a positive multiple of block_size";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_ALIAS: return "output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+}  // extern "C"

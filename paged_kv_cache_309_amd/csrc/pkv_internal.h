@@ -1,0 +1,60 @@
+// pkv_internal.h - what the C-ABI layer and the kernel translation units
+// share: the launch arguments and the launchers each kernel file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Threads per workgroup of the decode kernels: four wave64 wavefronts.
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = 4;
+
+struct DecodeArgs {
+  void *out;              // [S, Hq, D] storage type (single pass, reduce)
+  float *ws_o;            // [S, Hq, P, D] partial weighted sums (split)
+  float *ws_m;            // [S, Hq, P] partial maxima, log2 units (split)
+  float *ws_l;            // [S, Hq, P] partial sums of exponentials (split)
+  const void *q;          // [S, Hq, D]
+  const void *k_cache;    // [NB, Hkv, bs, D]
+  const void *v_cache;    // [NB, Hkv, bs/4, D, 4]
+  const int32_t *block_tables;  // [S, max_blocks]
+  const int32_t *context_lens;  // [S]
+  float scale_log2;       // softmax scale times log2(e)
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int max_blocks;
+  int block_size;
+  int part_tokens;        // tokens per partition (split); unused otherwise
+  int num_parts;          // partitions per sequence (1 for single pass)
+};
+
+struct CacheWriteArgs {
+  const void *k;          // [T, Hkv, D]
+  const void *v;          // [T, Hkv, D]
+  void *k_cache;
+  void *v_cache;
+  const int64_t *slot_mapping;  // [T]
+  int64_t num_tokens;
+  int num_kv_heads;
+  int num_blocks;
+};
+
+// Each returns the launch error (hipSuccess when enqueued).
+hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int head_dim,
+                                int block_size, bool split, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int head_dim,
+                              int block_size, bool split, hipStream_t st);
+hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
+                                   int head_dim, hipStream_t st);
+hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
+                                    int head_dim, int block_size,
+                                    hipStream_t st);
+
+}  // namespace pkv

@@ -1,0 +1,132 @@
+// reduce_and_cache.hip - the partition-reduce kernel of the split decode
+// and the cache-write scatter.
+#include "pkv_device.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// Partition reduce.  Partition p of (sequence s, head h) left its largest
+// logit m_p (log2 units), its sum of exponentials l_p = sum 2^(x - m_p) and
+// its un-normalised weighted sum o_p = sum 2^(x - m_p) v.  With M = max m_p:
+//     out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
+// the same rescaling the online softmax uses inside a partition, so the
+// result is the softmax over the whole context.  Partitions at or past
+// ceil(L / part_tokens) were empty and are not read.
+// One workgroup of D threads per (sequence, head).
+template <int DT, int D>
+__global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int Hq = a.num_heads;
+  int L = a.context_lens[s];
+  L = max(0, min(L, a.max_blocks * a.block_size));
+  const int np = min(a.num_parts, (L + a.part_tokens - 1) / a.part_tokens);
+  const size_t base = ((size_t)s * Hq + h) * a.num_parts;
+  const size_t orow = ((size_t)s * Hq + h) * D;
+  if (np <= 0) {
+    store_elem<DT>(a.out, orow + d, 0.f);
+    return;
+  }
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[base + p]);
+  float num = 0.f, den = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float f = fast_exp2(a.ws_m[base + p] - M);
+    num = fmaf(f, a.ws_o[(base + p) * D + d], num);
+    den = fmaf(f, a.ws_l[base + p], den);
+  }
+  store_elem<DT>(a.out, orow + d, num / den);
+}
+
+hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
+                                   int head_dim, hipStream_t st) {
+  dim3 grid(a.num_heads, a.num_seqs);
+#define PKV_REDUCE(DTV, DV) \
+  hipLaunchKernelGGL((partition_reduce_kernel<DTV, DV>), grid, dim3(DV), 0, st, a)
+  if (head_dim == 128) {
+    if (dtype == DT_F32) PKV_REDUCE(DT_F32, 128);
+    else if (dtype == DT_F16) PKV_REDUCE(DT_F16, 128);
+    else PKV_REDUCE(DT_BF16, 128);
+  } else {
+    if (dtype == DT_F32) PKV_REDUCE(DT_F32, 64);
+    else if (dtype == DT_F16) PKV_REDUCE(DT_F16, 64);
+    else PKV_REDUCE(DT_BF16, 64);
+  }
+#undef PKV_REDUCE
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Cache write.  Token i goes to slot = slot_mapping[i]: block slot / BS,
+// offset slot % BS.  One thread moves one 16-byte chunk of one (token,
+// KV head) key row - a single 16-byte store into the K tile - and the same
+// dims of the value row, which the token-grouped V layout spreads with a
+// stride of four elements.  Negative or out-of-pool slots write nothing.
+template <int DT, int D, int BS>
+__global__ void __launch_bounds__(256) reshape_and_cache_kernel(CacheWriteArgs a) {
+  constexpr int E = Elem<DT>::bytes;
+  constexpr int EPC = 16 / E;      // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;     // chunks per (token, head) row
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = a.num_tokens * a.num_kv_heads * CPR;
+  if (idx >= total) return;
+  const int chunk = (int)(idx % CPR);
+  const int64_t row = idx / CPR;          // token * Hkv + head
+  const int g = (int)(row % a.num_kv_heads);
+  const int64_t i = row / a.num_kv_heads;
+  const int64_t slot = a.slot_mapping[i];
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * BS) return;
+  const int64_t p = slot / BS;
+  const int o = (int)(slot % BS);
+  const size_t src = (size_t)row * D + chunk * EPC;
+  const size_t tile = ((size_t)p * a.num_kv_heads + g) * BS * D;
+
+  const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k) + src * E);
+  *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache) + (tile + (size_t)o * D + chunk * EPC) * E) = kx;
+
+  const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) + src * E);
+  const size_t vb = tile + (size_t)(o / 4) * 4 * D + (o % 4);
+  if constexpr (E == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      static_cast<uint32_t *>(a.v_cache)[vb + (size_t)(chunk * EPC + e) * 4] = vx[e];
+  } else {
+    uint16_t *vp = static_cast<uint16_t *>(a.v_cache);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wd = vx[e >> 1];
+      vp[vb + (size_t)(chunk * EPC + e) * 4] = (e & 1) ? (uint16_t)(wd >> 16) : (uint16_t)wd;
+    }
+  }
+}
+
+template <int DT, int D>
+static hipError_t launch_rac_d(const CacheWriteArgs &a, int block_size, hipStream_t st) {
+  constexpr int CPR = D / (16 / Elem<DT>::bytes);
+  const int64_t total = a.num_tokens * a.num_kv_heads * CPR;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (block_size == 16)
+    hipLaunchKernelGGL((reshape_and_cache_kernel<DT, D, 16>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((reshape_and_cache_kernel<DT, D, 32>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_rac_dt(const CacheWriteArgs &a, int head_dim, int block_size,
+                                hipStream_t st) {
+  return head_dim == 128 ? launch_rac_d<DT, 128>(a, block_size, st)
+                         : launch_rac_d<DT, 64>(a, block_size, st);
+}
+
+hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
+                                    int head_dim, int block_size,
+                                    hipStream_t st) {
+  if (a.num_tokens == 0) return hipSuccess;
+  switch (dtype) {
+    case DT_F32: return launch_rac_dt<DT_F32>(a, head_dim, block_size, st);
+    case DT_F16: return launch_rac_dt<DT_F16>(a, head_dim, block_size, st);
+    default: return launch_rac_dt<DT_BF16>(a, head_dim, block_size, st);
+  }
+}
+
+}  // namespace pkv

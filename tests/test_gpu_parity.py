@@ -1,0 +1,206 @@
+"""GPU parity on small and medium cases, every call through the C ABI.
+
+Sizes are ones the oracle finishes in well under a second, yet they span
+many 16-token tiles, several partitions and a ragged last block, with zero-
+and one-token sequences among them.  Unused pool blocks and the unused
+slots of last blocks hold NaN, so any read of a masked slot shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import (Dev, compare, host_bits, oracle_out, oracle_pool,
+                      pool_bits, to_f64, to_torch)
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, bs, Hq, Hkv, D, S, max_len (min_len 0)
+    ("f32", 16, 2, 2, 64, 6, 200),
+    ("f32", 32, 4, 4, 128, 5, 300),
+    ("f32", 16, 8, 2, 64, 4, 150),       # GQA on the vector kernel
+    ("f16", 16, 8, 8, 128, 7, 700),
+    ("f16", 32, 4, 4, 64, 5, 400),
+    ("f16", 16, 16, 2, 128, 6, 600),     # GQA, 8 heads per KV head
+    ("f16", 32, 12, 3, 64, 5, 500),      # GQA, 4 per KV head
+    ("bf16", 16, 4, 4, 128, 6, 900),
+    ("bf16", 32, 8, 8, 64, 4, 333),
+    ("bf16", 16, 64, 8, 128, 5, 800),    # the 70B-class head shape
+    ("bf16", 32, 32, 2, 128, 4, 500),    # 16 per KV head (widest MFMA group)
+    ("bf16", 16, 40, 2, 64, 3, 200),     # 20 per KV head: vector kernel
+    ("bf16", 16, 6, 3, 128, 5, 64),      # G = 2
+]
+
+
+def case(i, seed=0):
+    dtype, bs, Hq, Hkv, D, S, max_len = CASES[i]
+    return wl.random_case(1000 * i + seed, num_seqs=S, max_len=max_len,
+                          num_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                          block_size=bs, dtype=dtype, pool_factor=1.7)
+
+
+def print_case(tag, w):
+    print(f"[{tag}] {w.name} {w.dtype} bs={w.block_size} Hq={w.num_heads} "
+          f"Hkv={w.num_kv_heads} D={w.head_dim} lens={w.context_lens.tolist()}",
+          flush=True)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_cache_write_bit_exact(i):
+    """The whole pool after the GPU cache write equals the oracle's, bit for
+    bit, untouched slots included (they keep their NaN sentinel)."""
+    w = case(i)
+    print_case("rac", w)
+    dev = Dev(w)
+    kc0, vc0 = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
+                               w.head_dim, w.dtype)
+    kc_d, vc_d = dev.cache_from_host(kc0, vc0)
+    import paged_kv_cache_309_amd as pkv
+    kk, vv = to_torch(w.kv_k, w.dtype), to_torch(w.kv_v, w.dtype)
+    pkv.reshape_and_cache(kk, vv, kc_d, vc_d,
+                          torch.from_numpy(w.kv_slots).cuda())
+    torch.cuda.synchronize()
+    kc1, vc1 = oracle_pool(w)
+    assert np.array_equal(pool_bits(kc_d), host_bits(kc1))
+    assert np.array_equal(pool_bits(vc_d), host_bits(vc1))
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+@pytest.mark.parametrize("variant", ["single", "split64", "split_bs",
+                                     "split512"])
+def test_decode_matches_oracle(i, variant):
+    w = case(i)
+    print_case(f"decode {variant}", w)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    if variant == "single":
+        out = dev.decode(kd, vd)
+    else:
+        part = {"split64": 64, "split_bs": w.block_size, "split512": 512}[variant]
+        out = dev.decode(kd, vd, variant="split", partition=part)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    compare(got, want, w.dtype, f"case {i} {variant}")
+
+
+@pytest.mark.parametrize("i", [0, 3, 5, 9, 10])
+def test_round_trip_through_gpu_cache_write(i):
+    """Inputs written by the library's own cache write, then decoded."""
+    w = case(i, seed=1)
+    print_case("round trip", w)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_via_gpu_write()
+    compare(to_f64(dev.decode(kd, vd)), want, w.dtype, "single")
+    compare(to_f64(dev.decode(kd, vd, "split", 256)), want, w.dtype, "split")
+
+
+@pytest.mark.parametrize("i", [0, 4, 7, 9, 10, 11])
+def test_one_hot_probe_bit_exact(i):
+    """q = e_0, keys zero except k_j[0] = 16384 at one token j per sequence:
+    the weights are exactly 1 and 0, so out == v_j bit for bit, for the
+    single-pass and the split paths.  This pins the block-table indexing
+    exactly (any wrong tile, row or offset returns another token's value)."""
+    w = case(i, seed=2)
+    print_case("probe", w)
+    dev = Dev(w)
+    G = w.num_heads // w.num_kv_heads
+    q = np.zeros_like(w.q)
+    q[:, :, 0] = wl.f32_to_storage(np.float32([1.0]), w.dtype)[0]
+    big = wl.f32_to_storage(np.float32([16384.0]), w.dtype)[0]
+    qd = to_torch(q, w.dtype)
+    rng = np.random.default_rng(i)
+    Lmax = int(w.context_lens.max())
+    positions = sorted(set([0, 1, 15, 16, 17, 31, 32, Lmax - 1]
+                           + list(rng.integers(0, max(Lmax, 1), 12))))
+    for j in positions:
+        pos = np.minimum(j, np.maximum(w.context_lens - 1, 0))
+        kk = np.zeros_like(w.kv_k)
+        for s in range(w.num_seqs):
+            if w.context_lens[s] > 0:
+                kk[w.token_rows[s][pos[s]], :, 0] = big
+        kc, vc = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
+                                 w.head_dim, w.dtype)
+        oracle.reshape_and_cache(kk, w.kv_v, kc, vc, w.kv_slots,
+                                 w.num_kv_heads, w.head_dim, w.block_size,
+                                 w.num_blocks, w.dtype)
+        kd, vd = dev.cache_from_host(kc, vc)
+        for variant, part in (("single", 0), ("split", 64), ("split", 512)):
+            out = dev.decode(kd, vd, variant, part, q=qd)
+            got = out.cpu()
+            for s in range(w.num_seqs):
+                if w.context_lens[s] == 0:
+                    assert torch.all(got[s] == 0)
+                    continue
+                row = w.token_rows[s][pos[s]]
+                want = to_torch(w.kv_v[row], w.dtype, "cpu")  # [Hkv, D]
+                want = want.repeat_interleave(G, dim=0)
+                assert torch.equal(got[s].view(torch.int16 if got.element_size() == 2 else torch.int32),
+                                   want.view(torch.int16 if got.element_size() == 2 else torch.int32)), \
+                    (variant, part, j, s)
+
+
+@pytest.mark.parametrize("i", [1, 5, 8, 9])
+def test_physical_permutation_bitwise(i):
+    """Moving blocks around the pool (tables updated) leaves the GPU result
+    bit-identical: the arithmetic depends only on logical order."""
+    w = case(i, seed=3)
+    print_case("perm", w)
+    dev = Dev(w)
+    kc, vc = oracle_pool(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    base_s = dev.decode(kd, vd).cpu()
+    base_p = dev.decode(kd, vd, "split", 64).cpu()
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    bs = w.block_size
+    slots = np.where(w.kv_slots >= 0,
+                     perm[w.kv_slots // bs] * bs + w.kv_slots % bs, -1)
+    tables = np.where(w.block_tables >= 0,
+                      perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    kc2, vc2 = oracle.new_pool(w.num_blocks, w.num_kv_heads, bs, w.head_dim,
+                               w.dtype)
+    oracle.reshape_and_cache(w.kv_k, w.kv_v, kc2, vc2, slots, w.num_kv_heads,
+                             w.head_dim, bs, w.num_blocks, w.dtype)
+    kd2, vd2 = dev.cache_from_host(kc2, vc2)
+    t2 = torch.from_numpy(tables).cuda()
+    assert torch.equal(dev.decode(kd2, vd2, tables=t2).cpu(), base_s)
+    assert torch.equal(dev.decode(kd2, vd2, "split", 64, tables=t2).cpu(), base_p)
+
+
+def test_deterministic_run_to_run():
+    w = case(9, seed=4)
+    dev = Dev(w)
+    kc, vc = oracle_pool(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    a = dev.decode(kd, vd).cpu()
+    b = dev.decode(kd, vd).cpu()
+    c = dev.decode(kd, vd, "split", 128).cpu()
+    d = dev.decode(kd, vd, "split", 128).cpu()
+    assert torch.equal(a, b) and torch.equal(c, d)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_edge_contexts(dtype):
+    """Lengths 0, 1, exactly one block, one past a block, the table's
+    maximum; identical keys (mean of values) for one sequence."""
+    bs = 16
+    lens = [0, 1, 16, 17, 15, 64 * bs, 33, 0]
+    w = wl.build("edges", lens=lens, num_heads=8, num_kv_heads=2,
+                 head_dim=128, block_size=bs, dtype=dtype, seed=7,
+                 pool_factor=1.3, max_blocks_per_seq=64)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    for variant, part in (("single", 0), ("split", 16), ("split", 512)):
+        got = to_f64(dev.decode(kd, vd, variant, part))
+        compare(got, want, dtype, f"{variant}{part}")
+        assert np.all(got[0] == 0) and np.all(got[7] == 0)
+        # one token: the output is that token's value, exactly
+        v0 = to_f64(to_torch(w.kv_v[w.token_rows[1][0]], dtype))
+        assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
