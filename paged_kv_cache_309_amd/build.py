@@ -33,6 +33,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # no packed fp32 (v_pk_*_f32) instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+    # multiplies them with VALU instructions, which cannot work on AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -13,18 +13,25 @@
 //
 // One workgroup (4 wavefronts) per (sequence, KV head[, partition]); each
 // K/V tile is read from HBM once for all G heads.  Per 16-token tile a
-// wavefront issues D/32 v_mfma_f32_16x16x32 (keys as the A operand, 16
-// tokens x 32 dims per lane-group, queries as B, one head per column) and
-// 2*D/16 v_mfma_f32_16x16x16 (values as A: each lane holds 4 consecutive
-// tokens of one dim, which is what the token-grouped V layout stores
-// contiguously; probabilities as B).  The probabilities go in as a
-// high and a low half-precision part (p = hi + lo to about 16 bits), so the
-// value product keeps near-fp32 weights.
+// wavefront issues D/32 v_mfma_f32_16x16x32 for the logits (keys as the A
+// operand: 16 tokens x 32 dims, one token per lane-column; queries as B, one
+// head per column) and 2 x D/16 v_mfma_f32_16x16x16 for the values (values
+// as A: each lane holds four consecutive tokens of one dim, which the
+// token-grouped V layout stores contiguously; probabilities as B).
 //
-// The output of the QK product leaves lane l holding tokens 4*(l/16)+i of
-// head l%16, which is exactly the layout the PV product wants for its B
-// operand, so the probabilities never move between lanes.  Heads >= G are
-// padding: their logits are masked to -inf.
+// Lane layouts:
+//  * the logits come out as lane l holding tokens 4*(l/16)+i of head l%16,
+//    exactly the B operand layout of the value product, so probabilities
+//    never move between lanes;
+//  * the value product's row index m (= lane l%16 of the A operand) is
+//    mapped to dim 32*u + 2*m + j for n-tile 2*u + j, so that every lane's
+//    A operands of two consecutive n-tiles are one 16-byte chunk of the V
+//    tile, and one load instruction covers four 256-byte runs;
+//  * heads >= G are padding columns, masked to -inf.
+//
+// The probabilities enter the value product as a high and a low
+// half-precision part (p = hi + lo to about 16 significant bits), so the
+// weights keep near-fp32 precision.
 #include "pkv_device.h"
 
 namespace pkv {
@@ -40,10 +47,16 @@ template <> struct MfmaOps<DT_BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
         __builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
   }
-  // p -> (hi, lo) bit patterns with hi + lo ~= p
-  __device__ static __forceinline__ void split(float p, uint32_t &hi, uint32_t &lo) {
-    hi = from_f32<DT_BF16>(p);
-    lo = from_f32<DT_BF16>(p - __uint_as_float(hi << 16));
+  // two probabilities -> packed (hi, lo) bfloat16 pairs with hi + lo ~= p:
+  // hi keeps the top 16 bits of p, lo the top 16 bits of the remainder
+  __device__ static __forceinline__ void split2(float p0, float p1, uint32_t &hi,
+                                                uint32_t &lo) {
+    const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+    const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+    const uint32_t r0 = __float_as_uint(p0 - __uint_as_float(h0));
+    const uint32_t r1 = __float_as_uint(p1 - __uint_as_float(h1));
+    hi = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
+    lo = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
   }
 };
 
@@ -56,46 +69,48 @@ template <> struct MfmaOps<DT_F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(
         __builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
-  __device__ static __forceinline__ void split(float p, uint32_t &hi, uint32_t &lo) {
-    const _Float16 h = static_cast<_Float16>(p);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(p - static_cast<float>(h)));
+  __device__ static __forceinline__ void split2(float p0, float p1, uint32_t &hi,
+                                                uint32_t &lo) {
+    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+    const f16x2 r = __builtin_bit_cast(
+        f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(h.x),
+                                          p1 - static_cast<float>(h.y)));
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, r);
   }
 };
 
 template <int D>
 struct MfmaTile {
-  u32x4 k[D / 32];  // A operand of the QK products
-  u32x2 v[D / 16];  // A operand of the PV products
+  u32x4 k[D / 32];  // A operands of the logit products
+  u32x4 v[D / 32];  // A operands of two value products each
 };
-
-template <int DT, int D, int BS>
-__device__ __forceinline__ void load_mfma_tile(MfmaTile<D> &t, const char *kc,
-                                               const char *vc, size_t tile_elem,
-                                               int col, int grp) {
-  constexpr int E = 2;
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    t.k[kk] = *reinterpret_cast<const u32x4 *>(
-        kc + (tile_elem + (size_t)col * D + (kk * 4 + grp) * 8) * E);
-#pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt)
-    t.v[nt] = *reinterpret_cast<const u32x2 *>(
-        vc + (tile_elem + (size_t)grp * 4 * D + (nt * 16 + col) * 4) * E);
-}
 
 template <int DT, int D, int BS, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_mfma_kernel(DecodeArgs a) {
   using Ops = MfmaOps<DT>;
-  constexpr int SUBS = BS / 16;
-  constexpr int NT = D / 16;
+  using Tl = MfmaTile<D>;
+  constexpr int E = 2;
+  constexpr int KC = D / 32;   // logit MFMAs and V chunks per tile
+  constexpr int NT = D / 16;   // value n-tiles
 
-  const int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int g = blockIdx.x, part = blockIdx.z;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+
+  // LDS: the merge of the 4 wavefronts; before the loop it holds the sort
+  // keys of the longest-first order
+  __shared__ float sm_o[kDecodeWaves][16][D + 4];
+  __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
+  static_assert(sizeof(sm_o) >= kOrderMaxSeqs * sizeof(int), "order scratch");
+  const int s = SPLIT ? (int)blockIdx.y
+                      : longest_first_seq<kDecodeThreads>(
+                            a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,
+                            reinterpret_cast<int *>(&sm_o[0][0][0]));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
 
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks * BS));
@@ -111,11 +126,11 @@ decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Q^T operand: lane holds head `col`, dims (kk*4+grp)*8 .. +8
-  u32x4 qop[D / 32];
+  u32x4 qop[KC];
   {
-    const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * 2;
+    const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * E;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
+    for (int kk = 0; kk < KC; ++kk)
       qop[kk] = col < G ? *reinterpret_cast<const u32x4 *>(qp + (kk * 4 + grp) * 16)
                         : u32x4{0u, 0u, 0u, 0u};
   }
@@ -123,108 +138,108 @@ decode_mfma_kernel(DecodeArgs a) {
   const char *kc = static_cast<const char *>(a.k_cache);
   const char *vc = static_cast<const char *>(a.v_cache);
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
-  const unsigned nb = (unsigned)a.num_blocks;
 
   const int st_begin = tok_begin >> 4;
   const int st_end = (tok_end + 15) >> 4;
   const int n_tiles = st_end - st_begin;
   const int n_mine = n_tiles > w ? (n_tiles - w + 3) >> 2 : 0;
 
-  auto fetch_entries = [&](int n0) -> int {
-    const int n = n0 + lane;
-    if (n >= n_mine) return 0;
-    return trow[(st_begin + w + 4 * n) / SUBS];
-  };
-  auto tile_base = [&](int ent, int n) -> size_t {
-    const int phys = (unsigned)ent < nb ? ent : 0;
-    const int k = st_begin + w + 4 * n;
-    return ((size_t)phys * Hkv + g) * BS * D + (size_t)(k % SUBS) * 16 * D;
-  };
+  // lane offsets inside a tile, in bytes
+  const uint32_t koff = (uint32_t)(col * D * E + grp * 16);         // + kk*64
+  const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);     // + u*256
 
   float m = -INFINITY, l = 0.f;  // head `col`; l is this lane's share
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (n_mine > 0) {
-    int ent_cur = fetch_entries(0);
-    int ent_nxt = n_mine > 64 ? fetch_entries(64) : 0;
-    MfmaTile<D> cur, nxt;
-    load_mfma_tile<DT, D, BS>(cur, kc, vc,
-                              tile_base(__builtin_amdgcn_readlane(ent_cur, 0), 0), col, grp);
-    for (int n = 0; n < n_mine; ++n) {
-      const int n1 = n + 1;
-      if (n1 < n_mine) {
-        if ((n1 & 63) == 0) {
-          ent_cur = ent_nxt;
-          if (n1 + 64 < n_mine) ent_nxt = fetch_entries(n1 + 64);
-        }
-        load_mfma_tile<DT, D, BS>(
-            nxt, kc, vc, tile_base(__builtin_amdgcn_readlane(ent_cur, n1 & 63), n1), col, grp);
+  auto load = [&](Tl &t, size_t tile_bytes) {
+    const char *kp = kc + tile_bytes + koff;
+    const char *vp = vc + tile_bytes + voff;
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) t.k[kk] = load_stream16(kp + kk * 64);
+#pragma unroll
+    for (int u = 0; u < KC; ++u) t.v[u] = load_stream16(vp + u * 256);
+  };
+
+  auto compute = [&](Tl &t, int n) {
+    // S^T[token 4*grp+i][head col]
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[kk], sacc);
+
+    const int t0 = (st_begin + w + 4 * n) * 16 + 4 * grp;
+    const bool tail = (st_begin + w + 4 * n) * 16 + 16 > tok_end;
+    const int nvalid = tail ? max(0, min(4, tok_end - t0)) : 4;
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sc[i] = (i < nvalid && col < G) ? sacc[i] * a.scale_log2 : -INFINITY;
+    if (tail) {
+      // masked tokens' values may hold anything (NaN included): zero them
+      const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int u = 0; u < KC; ++u) {
+        t.v[u][0] &= m01;
+        t.v[u][1] &= m23;
+        t.v[u][2] &= m01;
+        t.v[u][3] &= m23;
       }
-
-      // S^T[token 4*grp+i][head col]
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) sacc = Ops::qk(cur.k[kk], qop[kk], sacc);
-
-      const int t0 = (st_begin + w + 4 * n) * 16 + 4 * grp;
-      const bool tail = (st_begin + w + 4 * n) * 16 + 16 > tok_end;
-      const int nvalid = tail ? max(0, min(4, tok_end - t0)) : 4;
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc[i] = (i < nvalid && col < G) ? sacc[i] * a.scale_log2 : -INFINITY;
-      if (tail) {
-        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          cur.v[nt][0] &= m01;
-          cur.v[nt][1] &= m23;
-        }
-      }
-
-      // running max of head `col` over the 4 lanes that share it
-      float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m, mb);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
-      l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-      m = m_new;
-
-      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-      Ops::split(p[0], h0, l0);
-      Ops::split(p[1], h1, l1);
-      Ops::split(p[2], h2, l2);
-      Ops::split(p[3], h3, l3);
-      const u32x2 phi = {h0 | (h1 << 16), h2 | (h3 << 16)};
-      const u32x2 plo = {l0 | (l1 << 16), l2 | (l3 << 16)};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 x = acc[nt] * alpha;
-        x = Ops::pv(cur.v[nt], phi, x);
-        x = Ops::pv(cur.v[nt], plo, x);
-        acc[nt] = x;
-      }
-      cur = nxt;
     }
-  }
+
+    // running maximum of head `col`, shared by the 4 lanes holding it; only
+    // moved (exactly, with the cross-lane max) when a logit exceeds it by
+    // more than the slack somewhere in the wave
+    const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (wave_any(mb > m + kRescaleSlack)) {
+      float mh = fmaxf(mb, __shfl_xor(mb, 16));
+      mh = fmaxf(mh, __shfl_xor(mh, 32));
+      const float m_new = fmaxf(m, mh);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+      l *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+      m = m_new;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+
+    uint32_t h01, l01, h23, l23;
+    Ops::split2(p[0], p[1], h01, l01);
+    Ops::split2(p[2], p[3], h23, l23);
+    const u32x2 phi = {h01, h23};
+    const u32x2 plo = {l01, l23};
+#pragma unroll
+    for (int u = 0; u < KC; ++u) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
+        acc[2 * u + j] = Ops::pv(va, phi, acc[2 * u + j]);
+        acc[2 * u + j] = Ops::pv(va, plo, acc[2 * u + j]);
+      }
+    }
+  };
+
+  if (n_mine > 0)
+    walk_tiles<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+                   (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
+                   load, compute);
 
   // ---- merge the 4 wavefronts through LDS ----
-  __shared__ float sm_o[kDecodeWaves][16][D + 4];
-  __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
+  // acc[2u+j][i] is dim 32u + 2(4*grp+i) + j of head col
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int u = 0; u < KC; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[w][col][nt * 16 + 4 * grp + i] = acc[nt][i];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sm_o[w][col][32 * u + 2 * (4 * grp + i) + j] = acc[2 * u + j][i];
   if (grp == 0) {
     sm_m[w][col] = m;
     sm_l[w][col] = lt;

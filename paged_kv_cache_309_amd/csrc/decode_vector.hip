@@ -28,16 +28,16 @@
 //  * q.k is a per-lane partial dot product reduced over the row with four
 //    DPP adds; each row keeps its own running max / sum / accumulator, so no
 //    lane talks to another row inside the loop;
-//  * the next tile's loads are issued before the current tile is computed,
-//    and block-table entries are fetched 64 tiles at a time, one per lane,
-//    then broadcast with readlane;
+//  * the next tile's loads are issued before the current tile is computed;
+//    the tile's address is a scalar, each lane's offset inside a tile is
+//    fixed for the whole loop;
 //  * at the end the 16 partial states (4 rows x 4 waves) are merged through
 //    LDS, each rescaled to the largest maximum.
 #include "pkv_device.h"
 
 namespace pkv {
 
-template <int DT, int D, int BS>
+template <int DT, int D>
 struct VecTile {
   static constexpr int E = Elem<DT>::bytes;
   static constexpr int DQ = D / 16;          // dims per lane on the K side
@@ -49,54 +49,29 @@ struct VecTile {
   uint32_t v[VW];
 };
 
-template <int DT, int D, int BS>
-__device__ __forceinline__ void load_vec_tile(VecTile<DT, D, BS> &t,
-                                              const char *kc, const char *vc,
-                                              size_t tile_elem, int r, int c) {
-  using Tl = VecTile<DT, D, BS>;
-  constexpr int E = Tl::E;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const char *p = kc + (tile_elem + (size_t)(4 * r + i) * D + c * Tl::DQ) * E;
-    if constexpr (Tl::KW == 2) {
-      const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
-      t.k[i][0] = x[0];
-      t.k[i][1] = x[1];
-    } else {
-#pragma unroll
-      for (int u = 0; u < Tl::KW / 4; ++u) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(p + 16 * u);
-        t.k[i][4 * u + 0] = x[0];
-        t.k[i][4 * u + 1] = x[1];
-        t.k[i][4 * u + 2] = x[2];
-        t.k[i][4 * u + 3] = x[3];
-      }
-    }
-  }
-  const char *pv = vc + (tile_elem + (size_t)r * 4 * D) * E + c * 16;
-#pragma unroll
-  for (int ii = 0; ii < Tl::VI; ++ii) {
-    const u32x4 x = *reinterpret_cast<const u32x4 *>(pv + ii * 256);
-    t.v[4 * ii + 0] = x[0];
-    t.v[4 * ii + 1] = x[1];
-    t.v[4 * ii + 2] = x[2];
-    t.v[4 * ii + 3] = x[3];
-  }
-}
-
 template <int DT, int D, int BS, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_vector_kernel(DecodeArgs a) {
-  using Tl = VecTile<DT, D, BS>;
+  using Tl = VecTile<DT, D>;
   constexpr int E = Tl::E;
-  constexpr int SUBS = BS / 16;
   constexpr int NACC = Tl::VI * Tl::DPV;  // == D / 16
 
-  const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int h = blockIdx.x, part = blockIdx.z;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane >> 4, c = lane & 15;
+
+  // LDS: the final merge of partial states; before the loop it holds the
+  // sort keys of the longest-first order
+  __shared__ float sm_acc[16][D];
+  __shared__ float sm_m[16], sm_l[16];
+  static_assert(sizeof(sm_acc) >= kOrderMaxSeqs * sizeof(int), "order scratch");
+  const int s = SPLIT ? (int)blockIdx.y
+                      : longest_first_seq<kDecodeThreads>(
+                            a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,
+                            reinterpret_cast<int *>(&sm_acc[0][0]));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63, r = lane >> 4, c = lane & 15;
 
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks * BS));
@@ -125,121 +100,125 @@ decode_vector_kernel(DecodeArgs a) {
   const char *kc = static_cast<const char *>(a.k_cache);
   const char *vc = static_cast<const char *>(a.v_cache);
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
-  const unsigned nb = (unsigned)a.num_blocks;
 
   const int st_begin = tok_begin >> 4;
   const int st_end = (tok_end + 15) >> 4;
   const int n_tiles = st_end - st_begin;
   const int n_mine = n_tiles > w ? (n_tiles - w + 3) >> 2 : 0;
 
-  // block-table entry of this wave's n-th tile, one n per lane
-  auto fetch_entries = [&](int n0) -> int {
-    const int n = n0 + lane;
-    if (n >= n_mine) return 0;
-    return trow[(st_begin + w + 4 * n) / SUBS];
-  };
-  auto tile_base = [&](int ent, int n) -> size_t {
-    const int phys = (unsigned)ent < nb ? ent : 0;
-    const int k = st_begin + w + 4 * n;
-    return ((size_t)phys * Hkv + g) * BS * D + (size_t)(k % SUBS) * 16 * D;
-  };
+  // lane offsets inside a tile, in bytes
+  const uint32_t koff = (uint32_t)((4 * r * D + c * Tl::DQ) * E);
+  const uint32_t voff = (uint32_t)(r * 4 * D * E + c * 16);
 
   float m = -INFINITY, l = 0.f;
   float acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
 
-  if (n_mine > 0) {
-    int ent_cur = fetch_entries(0);
-    int ent_nxt = n_mine > 64 ? fetch_entries(64) : 0;
-    Tl cur, nxt;
-    load_vec_tile<DT, D, BS>(cur, kc, vc,
-                             tile_base(__builtin_amdgcn_readlane(ent_cur, 0), 0), r, c);
-    for (int n = 0; n < n_mine; ++n) {
-      const int n1 = n + 1;
-      if (n1 < n_mine) {
-        if ((n1 & 63) == 0) {
-          ent_cur = ent_nxt;
-          if (n1 + 64 < n_mine) ent_nxt = fetch_entries(n1 + 64);
-        }
-        load_vec_tile<DT, D, BS>(
-            nxt, kc, vc, tile_base(__builtin_amdgcn_readlane(ent_cur, n1 & 63), n1), r, c);
-      }
-
-      // ---- logits of this row's four tokens (log2 units) ----
-      float sc[4];
+  auto load = [&](Tl &t, size_t tile_bytes) {
+    const char *kp = kc + tile_bytes + koff;
+    const char *vp = vc + tile_bytes + voff;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float d = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (Tl::KW == 2) {
+        const u32x2 x = load_stream8(kp + i * D * E);
+        t.k[i][0] = x[0];
+        t.k[i][1] = x[1];
+      } else {
 #pragma unroll
-        for (int e = 0; e < Tl::DQ; ++e) d = fmaf(qv[e], elem<DT>(cur.k[i], e), d);
-        sc[i] = row_sum16(d);
-      }
-      const int t0 = (st_begin + w + 4 * n) * 16 + 4 * r;  // first token of this row
-      if ((st_begin + w + 4 * n) * 16 + 16 > tok_end) {
-        // last tile: tokens at or past tok_end are masked; their V words
-        // may hold anything (NaN included) and are zeroed, not multiplied
-        const int nvalid = max(0, min(4, tok_end - t0));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i >= nvalid) sc[i] = -INFINITY;
-        if constexpr (E == 2) {
-          const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-          const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-          for (int u = 0; u < Tl::VW; u += 2) {
-            cur.v[u] &= m01;
-            cur.v[u + 1] &= m23;
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < Tl::VW; ++u)
-            if ((u & 3) >= nvalid) cur.v[u] = 0u;
+        for (int u = 0; u < Tl::KW / 4; ++u) {
+          const u32x4 x = load_stream16(kp + i * D * E + 16 * u);
+          t.k[i][4 * u + 0] = x[0];
+          t.k[i][4 * u + 1] = x[1];
+          t.k[i][4 * u + 2] = x[2];
+          t.k[i][4 * u + 3] = x[3];
         }
       }
-
-      // ---- online softmax update of this row's state ----
-      const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      const float m_new = fmaxf(m, mb);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
-      l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-      m = m_new;
-
-      // ---- weighted values ----
-#pragma unroll
-      for (int ii = 0; ii < Tl::VI; ++ii) {
-        if constexpr (E == 2) {
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const uint32_t *wv = &cur.v[4 * ii + 2 * k2];
-            float x = acc[2 * ii + k2] * alpha;
-            x = fmaf(p[0], elem<DT>(wv, 0), x);
-            x = fmaf(p[1], elem<DT>(wv, 1), x);
-            x = fmaf(p[2], elem<DT>(wv, 2), x);
-            x = fmaf(p[3], elem<DT>(wv, 3), x);
-            acc[2 * ii + k2] = x;
-          }
-        } else {
-          const uint32_t *wv = &cur.v[4 * ii];
-          float x = acc[ii] * alpha;
-          x = fmaf(p[0], elem<DT>(wv, 0), x);
-          x = fmaf(p[1], elem<DT>(wv, 1), x);
-          x = fmaf(p[2], elem<DT>(wv, 2), x);
-          x = fmaf(p[3], elem<DT>(wv, 3), x);
-          acc[ii] = x;
-        }
-      }
-      cur = nxt;
     }
+#pragma unroll
+    for (int ii = 0; ii < Tl::VI; ++ii) {
+      const u32x4 x = load_stream16(vp + ii * 256);
+      t.v[4 * ii + 0] = x[0];
+      t.v[4 * ii + 1] = x[1];
+      t.v[4 * ii + 2] = x[2];
+      t.v[4 * ii + 3] = x[3];
+    }
+  };
+
+  auto compute = [&](Tl &t, int n) {
+    // ---- logits of this row's four tokens (log2 units) ----
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < Tl::DQ; ++e) d = fmaf(qv[e], elem<DT>(t.k[i], e), d);
+      sc[i] = row_sum16(d);
+    }
+    const int tile_tok = (st_begin + w + 4 * n) * 16;
+    if (tile_tok + 16 > tok_end) {
+      // last tile: tokens at or past tok_end are masked; their V words may
+      // hold anything (NaN included) and are zeroed, not multiplied
+      const int nvalid = max(0, min(4, tok_end - tile_tok - 4 * r));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i >= nvalid) sc[i] = -INFINITY;
+      if constexpr (E == 2) {
+        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int u = 0; u < Tl::VW; u += 2) {
+          t.v[u] &= m01;
+          t.v[u + 1] &= m23;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < Tl::VW; ++u)
+          if ((u & 3) >= nvalid) t.v[u] = 0u;
+      }
+    }
+
+    // ---- online softmax: move the row's maximum only when a logit
+    //      exceeds it by more than the slack (wave-uniform branch) ----
+    const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (wave_any(mb > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mb);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) acc[i] *= alpha;
+      m = m_new;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // ---- weighted values ----
+#pragma unroll
+    for (int ii = 0; ii < Tl::VI; ++ii) {
+#pragma unroll
+      for (int k2 = 0; k2 < Tl::DPV; ++k2) {
+        const uint32_t *wv = &t.v[4 * ii + (E == 2 ? 2 * k2 : 0)];
+        float x = acc[ii * Tl::DPV + k2];
+        x = fmaf(p[0], elem<DT>(wv, 0), x);
+        x = fmaf(p[1], elem<DT>(wv, 1), x);
+        x = fmaf(p[2], elem<DT>(wv, 2), x);
+        x = fmaf(p[3], elem<DT>(wv, 3), x);
+        acc[ii * Tl::DPV + k2] = x;
+      }
+    }
+  };
+
+  if (n_mine > 0) {
+    constexpr size_t tile_elems = (size_t)16 * D;
+    walk_tiles<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+                   (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, tile_elems * E,
+                   load, compute);
   }
 
   // ---- merge the 16 partial states (4 rows x 4 waves) through LDS ----
-  __shared__ float sm_acc[16][D];
-  __shared__ float sm_m[16], sm_l[16];
   const int si = w * 4 + r;
 #pragma unroll
   for (int ii = 0; ii < Tl::VI; ++ii)

@@ -88,8 +88,119 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// K/V tiles are streamed: each is read once per decode step, so the loads
+// carry the non-temporal hint (measured on MI355X: random 4 KiB tile reads
+// reach about 6.8 TB/s with it and about 6.0 TB/s without).
+__device__ __forceinline__ u32x4 load_stream16(const void *p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 load_stream8(const void *p) {
+  return __builtin_nontemporal_load(static_cast<const u32x2 *>(p));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
+}
+
+// Rescaling threshold of the online softmax, in log2 units.  The running
+// maximum m of a softmax state is only moved when a new logit exceeds it by
+// more than this; until then the weights 2^(x - m) may reach 2^kRescaleSlack.
+// The final division by the running sum cancels the common factor, so the
+// result is the same softmax; the wave skips the rescale of its accumulators
+// on almost every tile.
+constexpr float kRescaleSlack = 8.0f;
+
+// True in every lane when any lane of the wavefront has `pred` set.
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+// Longest-first order of the single-pass grid.  Work items of one launch
+// differ in length by up to two orders of magnitude; the dispatcher starts
+// workgroups in grid order, so a long sequence that starts late stretches
+// the end of the kernel.  Workgroup row r therefore processes the sequence
+// of rank r in decreasing context length (ties in sequence order), computed
+// in every workgroup from context_lens: each thread owns up to
+// kOrderMaxSeqs / blockDim candidates and counts the keys larger than its
+// candidate's.  Keys pack (length, sequence) into one int:
+// (L << 10) | (1023 - s), unique, and larger for longer (then earlier)
+// sequences.  Above kOrderMaxSeqs sequences, or lengths of 2^21 tokens or
+// more, the grid order is kept.  `keys` is LDS scratch of kOrderMaxSeqs
+// ints; the result only chooses which workgroup does which sequence, never
+// the arithmetic.
+constexpr int kOrderMaxSeqs = 1024;
+
+template <int NT>
+__device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, int S,
+                                                 int max_tokens, int r, int *keys) {
+  if (S > kOrderMaxSeqs || max_tokens >= (1 << 21)) return r;
+  __shared__ int chosen;
+  const int tid = threadIdx.x;
+  const int Sp = (S + 3) & ~3;
+  for (int i = tid; i < Sp; i += NT) {
+    int L = i < S ? context_lens[i] : -1;
+    L = min(L, max_tokens);
+    keys[i] = i < S ? ((max(L, 0) << 10) | (1023 - i)) : -1;  // padding: smallest
+  }
+  __syncthreads();
+  for (int i = tid; i < S; i += NT) {
+    const int key = keys[i];
+    int rank = 0;
+    for (int j = 0; j < Sp; j += 4) {
+      const int4 k4 = *reinterpret_cast<const int4 *>(&keys[j]);
+      rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
+    }
+    if (rank == r) chosen = i;
+  }
+  __syncthreads();
+  return chosen;
+}
+
+// Walks the 16-token tiles a wavefront owns, with one tile of prefetch.
+//
+// The wave owns tiles k = k0 + 4n, n = 0 .. n_mine-1 (k0 = first tile of the
+// range + wave index); tile k lives in block table entry k / subs, at token
+// offset 16 * (k % subs) of that block.  Block-table entries are fetched
+// 64 at a time, one per lane, and broadcast with readlane, so the byte
+// offset of every tile is a wave-uniform (scalar) value.
+//
+//   load(tile, byte_offset)  issues the loads of one tile
+//   compute(tile, n)         consumes the n-th tile
+//
+// Two tile buffers alternate (no register copies between iterations).
+template <class Tile, class Load, class Compute>
+__device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mine,
+                                           int subs, unsigned num_blocks,
+                                           size_t head_off_bytes,
+                                           size_t block_bytes, size_t sub_bytes,
+                                           Load load, Compute compute) {
+  const int lane = threadIdx.x & 63;
+  auto fetch = [&](int n0) -> int {
+    const int n = n0 + lane;
+    return n < n_mine ? trow[(k0 + 4 * n) / subs] : 0;
+  };
+  int ent_cur = fetch(0);
+  int ent_nxt = n_mine > 64 ? fetch(64) : 0;
+  auto offset_of = [&](int n) -> size_t {
+    if ((n & 63) == 0 && n > 0) {
+      ent_cur = ent_nxt;
+      if (n + 64 < n_mine) ent_nxt = fetch(n + 64);
+    }
+    int phys = __builtin_amdgcn_readlane(ent_cur, n & 63);
+    phys = (unsigned)phys < num_blocks ? phys : 0;
+    const int k = k0 + 4 * n;
+    return (size_t)phys * block_bytes + head_off_bytes + (size_t)(k % subs) * sub_bytes;
+  };
+  Tile ta, tb;
+  load(ta, offset_of(0));
+  int n = 0;
+  for (; n + 1 < n_mine; n += 2) {
+    load(tb, offset_of(n + 1));
+    compute(ta, n);
+    if (n + 2 < n_mine) load(ta, offset_of(n + 2));
+    compute(tb, n + 1);
+  }
+  if (n < n_mine) compute(ta, n);
 }
 
 }  // namespace pkv
