@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--partition", type=int, default=512)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mode", default="decode", choices=["decode", "copy_blocks"],
+                   help="decode: the decode step (default); copy_blocks: the "
+                        "copy-on-write block copy")
+    p.add_argument("--pairs", type=int, default=2048,
+                   help="copy_blocks mode: block pairs copied per launch")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device copy "
                         "of this many MiB (to scale HBM counters)")
@@ -97,6 +102,8 @@ def main():
     import workloads as wl
 
     torch.cuda.set_device(0)
+    if args.mode == "copy_blocks":
+        return bench_copy_blocks(args)
     t0 = time.time()
     w = wl.CONFIGS[args.workload](args.seed)
     log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_heads} "
@@ -226,6 +233,68 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_copy_blocks(args):
+    """Copy-on-write block copies: `pairs` disjoint (source, destination)
+    block pairs of the shared-prefix workload's shape (32 KV heads, 16-token
+    blocks, head_dim 128, bf16: 128 KiB per block per pool), both pools."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_309_amd as pkv
+
+    nb, hkv, bs, d = 8192, 32, 16, 128
+    k_cache, v_cache = pkv.new_kv_cache(nb, hkv, bs, d, torch.bfloat16, fill=1.0)
+    rng = np.random.default_rng(args.seed)
+    perm = rng.permutation(nb)
+    n = min(args.pairs, nb // 2)
+    pairs = np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)
+    mapping = torch.from_numpy(pairs).cuda()
+    for _ in range(args.warmup):
+        pkv.copy_blocks(k_cache, v_cache, mapping)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        pkv.copy_blocks(k_cache, v_cache, mapping)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    block_bytes = hkv * bs * d * 2
+    moved = 2 * 2 * n * block_bytes            # K and V, read and written
+    gbs = moved / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kc = np.zeros(nb * hkv * bs * d, np.uint16)
+        vc = np.zeros_like(kc)
+        t1 = time.perf_counter()
+        oracle.copy_blocks(kc, vc, pairs, nb, "bf16")
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(moved / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt, 4),
+               "sample": f"the same {n} block pairs copied by the oracle"}
+    rec = {"metric": "copy_blocks effective GB/s (K and V blocks read and written)",
+           "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "copy_blocks", "pairs": n, "num_blocks": nb,
+                      "num_kv_heads": hkv, "block_size": bs, "head_dim": d,
+                      "block_bytes_per_pool": block_bytes},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": stored_traffic("copy_blocks_kernel", "copy_blocks"),
+                        "kernel": "copy_blocks_kernel",
+                        "algorithmic_bytes_per_launch": moved,
+                        "mean_launch_ms": round(ms, 5)},
+           "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
 
 

@@ -32,10 +32,10 @@ STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 
 _ERRORS = {
     1: "bad argument",
-    2: "block-table entry outside the pool",
+    2: "block index outside the pool",
     3: "context length beyond the block table",
     4: "slot beyond the pool",
-    5: "two tokens write one slot",
+    5: "two writes to one slot or block",
     6: "out of memory",
 }
 
@@ -76,6 +76,10 @@ def _load(path: str | None = None):
                 P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                 ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_copy_blocks.restype = ctypes.c_int
+            lib.oracle_copy_blocks.argtypes = [P, P, P, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int]
             lib.oracle_widen.restype = ctypes.c_int
             lib.oracle_widen.argtypes = [P, P, ctypes.c_int64, ctypes.c_int]
             if path is not None:
@@ -190,6 +194,18 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         bt.shape[1], DTYPES[dtype], sel_ptr, nsel,
         threads or default_threads()))
     return out
+
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, mapping,
+                num_blocks: int, dtype: str) -> None:
+    """Copy-on-write: block mapping[i][1] of both flat pools becomes a copy
+    of block mapping[i][0], in place."""
+    mp = np.ascontiguousarray(mapping, dtype=np.int64).reshape(-1, 2)
+    assert k_cache.size == v_cache.size and k_cache.size % max(num_blocks, 1) == 0
+    block_elems = k_cache.size // max(num_blocks, 1)
+    _check(_load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(mp),
+                                      mp.shape[0], num_blocks, block_elems,
+                                      DTYPES[dtype]))
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -385,3 +385,57 @@ int oracle_widen(const void *src, double *dst, int64_t n, int dtype) {
     dst[i] = load_elem(src, (size_t)i, dtype);
   return OR_OK;
 }
+
+/* ---- block copy (copy-on-write) ------------------------------------------ */
+
+/* Copy-on-write at block granularity: when a block held by several
+ * sequences must be written, the writer gets a fresh block holding a copy of
+ * it ("Why vLLM Uses PagedAttention", section "The bonus"; "PagedAttention:
+ * how vLLM manages the KV cache", section "Copy-on-write makes shared
+ * prefixes practical": only the block being written is copied).
+ *
+ * For each pair i, block mapping[2i+1] of both pools becomes a byte copy of
+ * block mapping[2i].  A block spans num_kv_heads * block_size * head_dim
+ * elements in either pool, whatever the layout inside it.  Rejected (no
+ * write): an index outside the pool, a destination that appears twice, or
+ * a destination that is also a source. */
+int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *mapping,
+                       int64_t num_pairs, int64_t num_blocks,
+                       int64_t block_elems, int dtype) {
+  if (num_pairs < 0 || num_blocks < 0 || block_elems <= 0 || dtype < OR_F32 ||
+      dtype > OR_BF16)
+    return OR_ERR_ARG;
+  unsigned char *dst_seen = calloc((size_t)num_blocks + 1, 1);
+  unsigned char *src_seen = calloc((size_t)num_blocks + 1, 1);
+  if (!dst_seen || !src_seen) {
+    free(dst_seen);
+    free(src_seen);
+    return OR_ERR_NOMEM;
+  }
+  int rc = OR_OK;
+  for (int64_t i = 0; i < num_pairs && rc == OR_OK; ++i) {
+    int64_t s = mapping[2 * i], d = mapping[2 * i + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+      rc = OR_ERR_TABLE;
+    else if (dst_seen[d])
+      rc = OR_ERR_SLOT_DUP;
+    else {
+      dst_seen[d] = 1;
+      src_seen[s] = 1;
+    }
+  }
+  for (int64_t i = 0; i < num_pairs && rc == OR_OK; ++i)
+    if (src_seen[mapping[2 * i + 1]])
+      rc = OR_ERR_SLOT_DUP;
+  free(dst_seen);
+  free(src_seen);
+  if (rc != OR_OK)
+    return rc;
+  const size_t bytes = (size_t)block_elems * (size_t)elem_bytes(dtype);
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    size_t s = (size_t)mapping[2 * i], d = (size_t)mapping[2 * i + 1];
+    memcpy((char *)k_cache + d * bytes, (const char *)k_cache + s * bytes, bytes);
+    memcpy((char *)v_cache + d * bytes, (const char *)v_cache + s * bytes, bytes);
+  }
+  return OR_OK;
+}

@@ -20,7 +20,8 @@ from ._lib import PkvDims, PkvError
 
 __all__ = ["reshape_and_cache", "paged_attention_decode",
            "paged_attention_decode_split", "split_workspace_bytes",
-           "new_kv_cache", "PkvError", "version"]
+           "new_kv_cache", "copy_blocks", "BlockManager", "PkvError",
+           "version"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
            torch.bfloat16: _lib.PKV_BF16}
@@ -129,6 +130,90 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         ctypes.byref(dims), _stream(stream)))
     return out
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy-on-write: block block_mapping[i, 1] of both caches becomes a
+    copy of block block_mapping[i, 0] (device int64 [n, 2])."""
+    NB, Hkv, bs, D = k_cache.shape
+    dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k_cache))
+    n = block_mapping.shape[0] if block_mapping.numel() else 0
+    _lib.check(_lib.lib().copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if n else None, n,
+        bs, ctypes.byref(dims), _stream(stream)))
+
+
+class BlockManager:
+    """Host block manager of the paged cache (free list, reference counts,
+    block tables, copy-on-write), a thin wrapper of the pkv_bm_* calls."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        import numpy as np
+        self._np = np
+        self._h = ctypes.c_void_p()
+        _lib.check(_lib.lib().pkv_bm_create(num_blocks, block_size,
+                                            ctypes.byref(self._h)))
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self) -> None:
+        if self._h:
+            _lib.lib().pkv_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        """Register a prompt of num_tokens; returns every token's slot."""
+        slots = self._np.empty(max(num_tokens, 1), self._np.int64)
+        _lib.check(_lib.lib().pkv_bm_add_sequence(
+            self._h, seq_id, num_tokens, slots.ctypes.data))
+        return slots[:num_tokens]
+
+    def fork(self, parent: int, child: int) -> None:
+        _lib.check(_lib.lib().pkv_bm_fork(self._h, parent, child))
+
+    def append_tokens(self, seq_ids):
+        """One new token per listed sequence: returns (slots [n] int64,
+        copy pairs [k, 2] int64 to run through copy_blocks first)."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        slots = np.empty(max(n, 1), np.int64)
+        pairs = np.empty((max(n, 1), 2), np.int64)
+        k = ctypes.c_int32(0)
+        _lib.check(_lib.lib().pkv_bm_append_tokens(
+            self._h, ids.ctypes.data, n, slots.ctypes.data, pairs.ctypes.data,
+            ctypes.byref(k)))
+        return slots[:n], pairs[:k.value]
+
+    def free_sequence(self, seq_id: int) -> None:
+        _lib.check(_lib.lib().pkv_bm_free_sequence(self._h, seq_id))
+
+    def batch_tables(self, seq_ids, max_blocks: int):
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        tables = np.empty((max(n, 1), max(max_blocks, 1)), np.int32)
+        lens = np.empty(max(n, 1), np.int32)
+        _lib.check(_lib.lib().pkv_bm_batch_tables(
+            self._h, ids.ctypes.data, n, max_blocks, tables.ctypes.data,
+            lens.ctypes.data))
+        return tables[:n, :max_blocks], lens[:n]
+
+    def num_free_blocks(self) -> int:
+        return _lib.lib().pkv_bm_num_free_blocks(self._h)
+
+    def refcount(self, block: int) -> int:
+        return _lib.lib().pkv_bm_refcount(self._h, block)
+
+    def num_tokens(self, seq_id: int) -> int:
+        return _lib.lib().pkv_bm_num_tokens(self._h, seq_id)
 
 
 # load (and fail loudly) at import

@@ -17,12 +17,18 @@ STATUS = {
     3: "PKV_ERR_BLOCK_SIZE", 4: "PKV_ERR_HEAD_DIM", 5: "PKV_ERR_HEADS",
     6: "PKV_ERR_SHAPE", 7: "PKV_ERR_ALIGN", 8: "PKV_ERR_PARTITION",
     9: "PKV_ERR_WORKSPACE", 10: "PKV_ERR_LAUNCH", 11: "PKV_ERR_ALIAS",
+    12: "PKV_ERR_NO_BLOCKS", 13: "PKV_ERR_UNKNOWN_SEQ",
+    14: "PKV_ERR_SEQ_EXISTS", 15: "PKV_ERR_CAPACITY",
 }
 
-# every symbol include/pkv.h declares
+# every function include/*.h declares
 EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "paged_attention_split_workspace_bytes",
-           "paged_attention_decode_split", "pkv_status_string", "pkv_version")
+           "paged_attention_decode_split", "pkv_status_string", "pkv_version",
+           "copy_blocks", "pkv_bm_create", "pkv_bm_destroy",
+           "pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_tokens",
+           "pkv_bm_free_sequence", "pkv_bm_batch_tables",
+           "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_bm_num_tokens")
 
 
 class PkvDims(ctypes.Structure):
@@ -58,6 +64,30 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_split.restype = I
     lib.paged_attention_decode_split.argtypes = [P, P, P, P, P, P, F, I, I, P,
                                                  ctypes.c_size_t, D, P]
+    lib.copy_blocks.restype = I
+    lib.copy_blocks.argtypes = [P, P, P, I, I, D, P]
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    lib.pkv_bm_create.restype = I
+    lib.pkv_bm_create.argtypes = [I32, I32, ctypes.POINTER(P)]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_add_sequence.restype = I
+    lib.pkv_bm_add_sequence.argtypes = [P, I64, I32, P]
+    lib.pkv_bm_fork.restype = I
+    lib.pkv_bm_fork.argtypes = [P, I64, I64]
+    lib.pkv_bm_append_tokens.restype = I
+    lib.pkv_bm_append_tokens.argtypes = [P, P, I32, P, P,
+                                         ctypes.POINTER(I32)]
+    lib.pkv_bm_free_sequence.restype = I
+    lib.pkv_bm_free_sequence.argtypes = [P, I64]
+    lib.pkv_bm_batch_tables.restype = I
+    lib.pkv_bm_batch_tables.argtypes = [P, P, I32, I32, P, P]
+    lib.pkv_bm_num_free_blocks.restype = I32
+    lib.pkv_bm_num_free_blocks.argtypes = [P]
+    lib.pkv_bm_refcount.restype = I32
+    lib.pkv_bm_refcount.argtypes = [P, I32]
+    lib.pkv_bm_num_tokens.restype = I32
+    lib.pkv_bm_num_tokens.argtypes = [P, I64]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_version.restype = I

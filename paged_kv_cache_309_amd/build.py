@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "decode_vector.hip", "decode_mfma.hip",
-           "reduce_and_cache.hip"]
+           "reduce_and_cache.hip", "copy_blocks.hip", "block_manager.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(OBJ_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [cc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
                os.path.join(CSRC, src), "-o", obj]

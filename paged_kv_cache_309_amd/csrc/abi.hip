@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "pkv.h"
+#include "pkv_blocks.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -233,6 +234,38 @@ int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+int copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
+                int num_pairs, int block_size, const pkv_dims *dims,
+                pkv_stream_t stream) {
+  if (!dims) return PKV_ERR_NULL;
+  if (dims->dtype < PKV_F32 || dims->dtype > PKV_BF16) return PKV_ERR_DTYPE;
+  if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
+  if (dims->head_dim != 64 && dims->head_dim != 128) return PKV_ERR_HEAD_DIM;
+  if (dims->num_kv_heads <= 0) return PKV_ERR_HEADS;
+  if (num_pairs < 0 || dims->num_blocks < 0) return PKV_ERR_SHAPE;
+  const u128 bb = (u128)dims->num_kv_heads * (u128)block_size * (u128)dims->head_dim *
+                  (u128)elem_bytes(dims->dtype);
+  const u128 cb = bb * (u128)dims->num_blocks;
+  if (cb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned(block_mapping, 8))
+    return PKV_ERR_ALIGN;
+  if (overlap(k_cache, (size_t)cb, v_cache, (size_t)cb) ||
+      overlap(block_mapping, (size_t)num_pairs * 16, k_cache, (size_t)cb) ||
+      overlap(block_mapping, (size_t)num_pairs * 16, v_cache, (size_t)cb))
+    return PKV_ERR_ALIAS;
+  pkv::CopyBlocksArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_mapping = block_mapping;
+  a.block_bytes = (int64_t)bb;
+  a.num_blocks = dims->num_blocks;
+  const hipError_t err =
+      pkv::launch_copy_blocks(a, num_pairs, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
 const char *pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "ok";
@@ -247,6 +280,10 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_ALIAS: return "output overlaps an input";
+    case PKV_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+    case PKV_ERR_SEQ_EXISTS: return "sequence id already in use";
+    case PKV_ERR_CAPACITY: return "output buffer too small";
     default: return "unknown status";
   }
 }

@@ -46,6 +46,14 @@ struct CacheWriteArgs {
   int num_blocks;
 };
 
+struct CopyBlocksArgs {
+  void *k_cache;
+  void *v_cache;
+  const int64_t *block_mapping;  // [num_pairs, 2] (source, destination)
+  int64_t block_bytes;           // bytes of one block in one pool
+  int num_blocks;
+};
+
 // Each returns the launch error (hipSuccess when enqueued).
 hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int head_dim,
                                 int block_size, bool split, hipStream_t st);
@@ -56,5 +64,7 @@ hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
 hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
                                     int head_dim, int block_size,
                                     hipStream_t st);
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, int num_pairs,
+                              hipStream_t st);
 
 }  // namespace pkv
