@@ -69,7 +69,9 @@ typedef struct ihipStream_t *pkv_stream_t;
 typedef enum pkv_dtype {
   PKV_F32 = 0,  /* IEEE binary32 */
   PKV_F16 = 1,  /* IEEE binary16 */
-  PKV_BF16 = 2  /* bfloat16 */
+  PKV_BF16 = 2, /* bfloat16 */
+  PKV_E4M3 = 3  /* 8-bit E4M3 cache elements: only copy_blocks takes it in
+                   dims->dtype (the *_fp8 calls imply it for their caches) */
 } pkv_dtype;
 
 typedef enum pkv_status {
@@ -85,7 +87,8 @@ typedef enum pkv_status {
                               block_size */
   PKV_ERR_WORKSPACE = 9,   /* workspace NULL or smaller than required */
   PKV_ERR_LAUNCH = 10,     /* the HIP runtime rejected a kernel launch */
-  PKV_ERR_ALIAS = 11       /* out overlaps an input */
+  PKV_ERR_ALIAS = 11,      /* out overlaps an input */
+  PKV_ERR_SCALE = 16       /* a dequantisation scale not finite and > 0 */
 } pkv_status;
 
 /* Sizes of one call.  Fields a call does not use are ignored. */
@@ -192,6 +195,46 @@ int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
                                  int block_size, int partition_size,
                                  void *workspace, size_t workspace_bytes,
                                  const pkv_dims *dims, pkv_stream_t stream);
+
+/* ---- 8-bit (E4M3) caches ----------------------------------------------
+ * Lower-precision cache formats reduce the bytes per element ("PagedAttention:
+ * how vLLM manages the KV cache", section "Keep the tensor formula beside the
+ * allocator model"); on this bandwidth-bound path that halves the bytes read
+ * per decode step.  The caches then hold one byte per element - the OCP
+ * 8-bit float E4M3 (sign, 4 exponent bits with bias 7, 3 fraction bits, no
+ * infinity, 0x7f/0xff NaN, largest finite 448) - in the same layouts as
+ * above, and each pool has one per-tensor scale: a stored code c stands for
+ * the value e4m3(c) * scale.  q, out, k and v keep dims->dtype.
+ *
+ * reshape_and_cache_fp8: element x is stored as the E4M3 value nearest to
+ * x / scale (the quotient in IEEE single precision; ties to the even
+ * fraction; magnitudes of 448 and beyond saturate to +-448; NaN stays NaN).
+ * paged_attention_decode_fp8 / _split_fp8: attention over the dequantised
+ * keys and values; the key scale multiplies the logits and the value scale
+ * the output, both in fp32.  The grouped-query matrix-core path needs a
+ * 16-bit dims->dtype (fp32 q with Hq/Hkv in 2..16 returns PKV_ERR_DTYPE).
+ * Scales must be finite and > 0 (else PKV_ERR_SCALE).  Everything else is
+ * as for the calls above. */
+int reshape_and_cache_fp8(const void *k, const void *v, void *k_cache,
+                          void *v_cache, const int64_t *slot_mapping,
+                          int num_tokens, int block_size, float k_scale,
+                          float v_scale, const pkv_dims *dims,
+                          pkv_stream_t stream);
+
+int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, float scale,
+                               int block_size, float k_scale, float v_scale,
+                               const pkv_dims *dims, pkv_stream_t stream);
+
+int paged_attention_decode_split_fp8(void *out, const void *q,
+                                     const void *k_cache, const void *v_cache,
+                                     const int32_t *block_tables,
+                                     const int32_t *context_lens, float scale,
+                                     int block_size, int partition_size,
+                                     void *workspace, size_t workspace_bytes,
+                                     float k_scale, float v_scale,
+                                     const pkv_dims *dims, pkv_stream_t stream);
 
 /* A static, human-readable description of a status code. */
 const char *pkv_status_string(int status);

@@ -42,7 +42,8 @@ enum {
  * For each pair i, block block_mapping[2i+1] of k_cache and of v_cache
  * becomes a copy of block block_mapping[2i] (all KV heads, all slots, raw
  * bits).  block_mapping: device int64 [num_pairs, 2] (source, destination).
- * Uses dims->num_kv_heads, head_dim, num_blocks, dtype.
+ * Uses dims->num_kv_heads, head_dim, num_blocks, dtype (PKV_E4M3 for the
+ * 8-bit caches).
  * Preconditions (device data, not checked): destinations pairwise distinct
  * and none of them a source.  A pair with an index outside the pool copies
  * nothing.  Asynchronous on `stream`; returns a pkv_status.

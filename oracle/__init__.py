@@ -27,8 +27,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "paged_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libpaged_oracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16,
+           "fp8": np.uint8}
 
 _ERRORS = {
     1: "bad argument",
@@ -76,6 +77,19 @@ def _load(path: str | None = None):
                 P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                 ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_paged_decode_q.restype = ctypes.c_int
+            lib.oracle_paged_decode_q.argtypes = [
+                P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                ctypes.c_float, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_reshape_and_cache_fp8.restype = ctypes.c_int
+            lib.oracle_reshape_and_cache_fp8.argtypes = [
+                P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                ctypes.c_float, ctypes.c_int]
+            lib.oracle_e4m3_encode.restype = ctypes.c_int
+            lib.oracle_e4m3_encode.argtypes = [P, P, ctypes.c_int64]
             lib.oracle_copy_blocks.restype = ctypes.c_int
             lib.oracle_copy_blocks.argtypes = [P, P, P, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_int64,
@@ -132,7 +146,9 @@ def new_pool(num_blocks: int, num_kv_heads: int, block_size: int,
     st = STORAGE[dtype]
     if fill == "zero":
         return np.zeros(n, st), np.zeros(n, st)
-    if dtype == "bf16":
+    if dtype == "fp8":
+        pat = np.uint8(0x7F)
+    elif dtype == "bf16":
         pat = np.uint16(0x7FC1)
     elif dtype == "f16":
         pat = np.float16(np.nan)
@@ -168,12 +184,16 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                  block_tables: np.ndarray, context_lens: np.ndarray,
                  scale: float, block_size: int, num_kv_heads: int,
                  num_blocks: int, dtype: str, sel=None,
-                 threads: int | None = None) -> np.ndarray:
+                 threads: int | None = None, cache_dtype: str | None = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode attention in float64.
 
-    q: [S, Hq, D] storage array.  Returns [S, Hq, D] float64, or, when
-    ``sel`` is an [N, 2] array of (seq, head) pairs, [N, D] float64.
+    q: [S, Hq, D] storage array of `dtype`; the caches hold `cache_dtype`
+    (default: `dtype`) and dequantise as element * k_scale / * v_scale.
+    Returns [S, Hq, D] float64, or, when ``sel`` is an [N, 2] array of
+    (seq, head) pairs, [N, D] float64.
     """
+    cache_dtype = cache_dtype or dtype
     st = STORAGE[dtype]
     q = np.ascontiguousarray(q, dtype=st)
     S, Hq, D = q.shape
@@ -188,11 +208,41 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         nsel = sel_arr.shape[0]
         out = np.empty((nsel, D), np.float64)
         sel_ptr = _ptr(sel_arr)
-    _check(_load().oracle_paged_decode(
+    assert k_cache.dtype == STORAGE[cache_dtype]
+    _check(_load().oracle_paged_decode_q(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
         float(scale), block_size, S, Hq, num_kv_heads, D, num_blocks,
-        bt.shape[1], DTYPES[dtype], sel_ptr, nsel,
-        threads or default_threads()))
+        bt.shape[1], DTYPES[dtype], DTYPES[cache_dtype], float(k_scale),
+        float(v_scale), sel_ptr, nsel, threads or default_threads()))
+    return out
+
+
+def reshape_and_cache_fp8(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray,
+                          v_cache: np.ndarray, slot_mapping: np.ndarray,
+                          num_kv_heads: int, head_dim: int, block_size: int,
+                          num_blocks: int, in_dtype: str, k_scale: float,
+                          v_scale: float) -> None:
+    """Quantising cache write into E4M3 pools (uint8 codes), in place."""
+    st = STORAGE[in_dtype]
+    k = np.ascontiguousarray(k, dtype=st)
+    v = np.ascontiguousarray(v, dtype=st)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    n = num_blocks * num_kv_heads * block_size * head_dim
+    assert k_cache.size == n and v_cache.size == n
+    T = slots.shape[0]
+    assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    _check(_load().oracle_reshape_and_cache_fp8(
+        _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slots), T,
+        num_kv_heads, head_dim, block_size, num_blocks, DTYPES[in_dtype],
+        float(k_scale), float(v_scale), default_threads()))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """The oracle's own float32 -> E4M3 encoding (uint8 codes)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _check(_load().oracle_e4m3_encode(_ptr(x), _ptr(out), x.size))
     return out
 
 

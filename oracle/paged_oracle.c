@@ -63,7 +63,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8 = 3 };
 
 enum {
   OR_OK = 0,
@@ -102,18 +102,74 @@ static double bf16_bits_to_double(uint16_t b) {
   return (double)f;
 }
 
+/* 8-bit float E4M3 ("FN" variant of the OCP 8-bit formats), written out
+ * from the format's definition: sign bit, 4 exponent bits (bias 7), 3
+ * fraction bits; exponent 0 encodes subnormals fr * 2^-9; there is no
+ * infinity, and exponent 15 with fraction 7 is NaN, so the largest finite
+ * value is 1.75 * 2^8 = 448. */
+static double e4m3_bits_to_double(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int ex = (b >> 3) & 0xf;
+  int fr = b & 7;
+  double v;
+  if (ex == 0xf && fr == 7)
+    return NAN;
+  if (ex == 0)
+    v = ldexp((double)fr, -9);
+  else
+    v = ldexp((double)(8 + fr), ex - 10); /* (1 + fr/8) * 2^(ex-7) */
+  return sign ? -v : v;
+}
+
+/* Nearest E4M3 value of a float, ties to the even fraction; magnitudes
+ * beyond the largest finite value saturate to +-448; NaN -> NaN (0x7f).
+ * The candidates come from the definition: the representable non-negative
+ * values are e4m3_bits_to_double(0 .. 126), increasing with the code, and
+ * the code just below a value is found by bisection over them. */
+static uint8_t e4m3_encode(float y) {
+  if (isnan(y))
+    return 0x7f;
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  if (a >= 448.0)
+    return sign | 0x7e;
+  /* largest code whose value is <= a: value(lo) <= a < value(hi) */
+  int lo = 0, hi = 126;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (e4m3_bits_to_double((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  if (e4m3_bits_to_double((uint8_t)hi) <= a)
+    lo = hi;
+  int code = lo;
+  if (lo < 126) {
+    double vlo = e4m3_bits_to_double((uint8_t)lo);
+    double vhi = e4m3_bits_to_double((uint8_t)(lo + 1));
+    if (a - vlo > vhi - a || (a - vlo == vhi - a && (lo & 1)))
+      code = lo + 1;
+  }
+  return sign | (uint8_t)code;
+}
+
 static double load_elem(const void *base, size_t idx, int dtype) {
   switch (dtype) {
   case OR_F32:
     return (double)((const float *)base)[idx];
   case OR_F16:
     return half_bits_to_double(((const uint16_t *)base)[idx]);
+  case OR_FP8:
+    return e4m3_bits_to_double(((const uint8_t *)base)[idx]);
   default:
     return bf16_bits_to_double(((const uint16_t *)base)[idx]);
   }
 }
 
-static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : 2; }
+static int elem_bytes(int dtype) {
+  return dtype == OR_F32 ? 4 : (dtype == OR_FP8 ? 1 : 2);
+}
 
 /* ---- pool addressing ---------------------------------------------------- */
 
@@ -193,7 +249,9 @@ struct decode_job {
   double scale;
   int block_size, num_seqs, num_heads, num_kv_heads, head_dim;
   int64_t num_blocks;
-  int max_blocks_per_seq, dtype;
+  int max_blocks_per_seq, dtype; /* dtype: of the caches */
+  int q_dtype;                     /* of q */
+  double k_scale, v_scale;         /* dequantisation scales of the caches */
   const int32_t *sel; /* optional (seq, head) pairs */
   int64_t num_items;
   int num_threads;
@@ -232,11 +290,12 @@ static int decode_one(const struct decode_job *jb, int s, int h, double *out) {
     }
     double dot = 0.0;
     for (int d = 0; d < hd; ++d)
-      dot += load_elem(jb->q, qbase + d, jb->dtype) *
-             load_elem(jb->k_cache,
-                       k_index((size_t)p, (size_t)g, (size_t)o, (size_t)d, hkv,
-                               (size_t)bs, (size_t)hd),
-                       jb->dtype);
+      dot += load_elem(jb->q, qbase + d, jb->q_dtype) *
+             (load_elem(jb->k_cache,
+                        k_index((size_t)p, (size_t)g, (size_t)o, (size_t)d, hkv,
+                                (size_t)bs, (size_t)hd),
+                        jb->dtype) *
+              jb->k_scale);
     x[t] = jb->scale * dot;
   }
 
@@ -254,10 +313,11 @@ static int decode_one(const struct decode_job *jb, int s, int h, double *out) {
     double w = exp(x[t] - m);
     z += w;
     for (int d = 0; d < hd; ++d)
-      out[d] += w * load_elem(jb->v_cache,
-                              v_index((size_t)p, (size_t)g, (size_t)o,
-                                      (size_t)d, hkv, (size_t)bs, (size_t)hd),
-                              jb->dtype);
+      out[d] += w * (load_elem(jb->v_cache,
+                               v_index((size_t)p, (size_t)g, (size_t)o,
+                                       (size_t)d, hkv, (size_t)bs, (size_t)hd),
+                               jb->dtype) *
+                     jb->v_scale);
   }
   for (int d = 0; d < hd; ++d)
     out[d] /= z;
@@ -301,17 +361,23 @@ static void *decode_worker(void *argp) {
  * block_tables: [num_seqs, max_blocks_per_seq]; context_lens: [num_seqs].
  * The items are spread over `num_threads` POSIX threads; every item is
  * computed on its own, so the result does not depend on the thread count. */
-int oracle_paged_decode(double *out, const void *q, const void *k_cache,
-                        const void *v_cache, const int32_t *block_tables,
-                        const int32_t *context_lens, float scale,
-                        int block_size, int num_seqs, int num_heads,
-                        int num_kv_heads, int head_dim, int64_t num_blocks,
-                        int max_blocks_per_seq, int dtype, const int32_t *sel,
-                        int64_t num_sel, int num_threads) {
+/* The general form: q in q_dtype, caches in cache_dtype holding values
+ * that dequantise as element * k_scale (keys) and element * v_scale
+ * (values).  Attention is that of the dequantised K and V. */
+int oracle_paged_decode_q(double *out, const void *q, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, float scale,
+                          int block_size, int num_seqs, int num_heads,
+                          int num_kv_heads, int head_dim, int64_t num_blocks,
+                          int max_blocks_per_seq, int q_dtype, int cache_dtype,
+                          float k_scale, float v_scale, const int32_t *sel,
+                          int64_t num_sel, int num_threads) {
+  const int dtype = cache_dtype;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0 ||
       block_size % 4 != 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
-      dtype < OR_F32 || dtype > OR_BF16 || num_threads <= 0)
+      dtype < OR_F32 || dtype > OR_FP8 || q_dtype < OR_F32 ||
+      q_dtype > OR_BF16 || num_threads <= 0)
     return OR_ERR_ARG;
   struct decode_job jb;
   memset(&jb, 0, sizeof jb);
@@ -330,6 +396,9 @@ int oracle_paged_decode(double *out, const void *q, const void *k_cache,
   jb.num_blocks = num_blocks;
   jb.max_blocks_per_seq = max_blocks_per_seq;
   jb.dtype = dtype;
+  jb.q_dtype = q_dtype;
+  jb.k_scale = (double)k_scale;
+  jb.v_scale = (double)v_scale;
   jb.sel = sel;
   jb.num_items = sel ? num_sel : (int64_t)num_seqs * num_heads;
   if (sel) {
@@ -376,10 +445,27 @@ int oracle_paged_decode(double *out, const void *q, const void *k_cache,
   return jb.status;
 }
 
+/* q and caches of one type, no scaling. */
+int oracle_paged_decode(double *out, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, float scale,
+                        int block_size, int num_seqs, int num_heads,
+                        int num_kv_heads, int head_dim, int64_t num_blocks,
+                        int max_blocks_per_seq, int dtype, const int32_t *sel,
+                        int64_t num_sel, int num_threads) {
+  if (dtype == OR_FP8)
+    return OR_ERR_ARG;
+  return oracle_paged_decode_q(out, q, k_cache, v_cache, block_tables,
+                               context_lens, scale, block_size, num_seqs,
+                               num_heads, num_kv_heads, head_dim, num_blocks,
+                               max_blocks_per_seq, dtype, dtype, 1.0f, 1.0f,
+                               sel, num_sel, num_threads);
+}
+
 /* Widen n stored elements to double with the decoders above; exported so
  * the decoders themselves can be checked against a library conversion. */
 int oracle_widen(const void *src, double *dst, int64_t n, int dtype) {
-  if (n < 0 || dtype < OR_F32 || dtype > OR_BF16)
+  if (n < 0 || dtype < OR_F32 || dtype > OR_FP8)
     return OR_ERR_ARG;
   for (int64_t i = 0; i < n; ++i)
     dst[i] = load_elem(src, (size_t)i, dtype);
@@ -403,7 +489,7 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *mapping,
                        int64_t num_pairs, int64_t num_blocks,
                        int64_t block_elems, int dtype) {
   if (num_pairs < 0 || num_blocks < 0 || block_elems <= 0 || dtype < OR_F32 ||
-      dtype > OR_BF16)
+      dtype > OR_FP8)
     return OR_ERR_ARG;
   unsigned char *dst_seen = calloc((size_t)num_blocks + 1, 1);
   unsigned char *src_seen = calloc((size_t)num_blocks + 1, 1);
@@ -437,5 +523,111 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *mapping,
     memcpy((char *)k_cache + d * bytes, (const char *)k_cache + s * bytes, bytes);
     memcpy((char *)v_cache + d * bytes, (const char *)v_cache + s * bytes, bytes);
   }
+  return OR_OK;
+}
+
+/* ---- 8-bit cache ----------------------------------------------------------
+ * Lower-precision cache formats reduce the bytes per element ("PagedAttention:
+ * how vLLM manages the KV cache", section "Keep the tensor formula beside the
+ * allocator model").  The cache write of an E4M3 cache stores, for every
+ * element, e4m3_encode(x / scale) with x / scale the float quotient (IEEE
+ * single precision, as the device computes it); slots and layouts are those
+ * of the plain cache write. */
+struct fp8_write_job {
+  const void *k, *v;
+  void *k_cache, *v_cache;
+  const int64_t *slot_mapping;
+  int64_t num_tokens;
+  int num_kv_heads, head_dim, block_size, in_dtype;
+  float k_scale, v_scale;
+  int num_threads;
+};
+
+struct fp8_write_arg {
+  struct fp8_write_job *jb;
+  int tid;
+};
+
+static void *fp8_write_worker(void *argp) {
+  struct fp8_write_arg *wa = argp;
+  const struct fp8_write_job *jb = wa->jb;
+  const size_t hkv = (size_t)jb->num_kv_heads, hd = (size_t)jb->head_dim,
+               bs = (size_t)jb->block_size;
+  for (int64_t i = wa->tid; i < jb->num_tokens; i += jb->num_threads) {
+    int64_t s = jb->slot_mapping[i];
+    if (s < 0)
+      continue;
+    size_t p = (size_t)(s / jb->block_size), o = (size_t)(s % jb->block_size);
+    for (size_t g = 0; g < hkv; ++g) {
+      for (size_t d = 0; d < hd; ++d) {
+        size_t src = ((size_t)i * hkv + g) * hd + d;
+        float xk = (float)load_elem(jb->k, src, jb->in_dtype);
+        float xv = (float)load_elem(jb->v, src, jb->in_dtype);
+        ((uint8_t *)jb->k_cache)[k_index(p, g, o, d, hkv, bs, hd)] =
+            e4m3_encode(xk / jb->k_scale);
+        ((uint8_t *)jb->v_cache)[v_index(p, g, o, d, hkv, bs, hd)] =
+            e4m3_encode(xv / jb->v_scale);
+      }
+    }
+  }
+  return NULL;
+}
+
+int oracle_reshape_and_cache_fp8(const void *k, const void *v, void *k_cache,
+                                 void *v_cache, const int64_t *slot_mapping,
+                                 int64_t num_tokens, int num_kv_heads,
+                                 int head_dim, int block_size,
+                                 int64_t num_blocks, int in_dtype,
+                                 float k_scale, float v_scale,
+                                 int num_threads) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 || num_blocks < 0 || in_dtype < OR_F32 ||
+      in_dtype > OR_BF16)
+    return OR_ERR_ARG;
+  const int64_t nslots = num_blocks * (int64_t)block_size;
+  unsigned char *seen = calloc((size_t)(nslots / 8 + 1), 1);
+  if (!seen)
+    return OR_ERR_NOMEM;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t s = slot_mapping[i];
+    if (s < 0)
+      continue;
+    if (s >= nslots || (seen[s / 8] & (1u << (s % 8)))) {
+      free(seen);
+      return s >= nslots ? OR_ERR_SLOT_RANGE : OR_ERR_SLOT_DUP;
+    }
+    seen[s / 8] |= (unsigned char)(1u << (s % 8));
+  }
+  free(seen);
+  struct fp8_write_job jb = {k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                             num_kv_heads, head_dim, block_size, in_dtype,
+                             k_scale, v_scale, num_threads};
+  /* the slots are distinct (checked above), so threads that take disjoint
+   * tokens write disjoint bytes */
+  pthread_t th[64];
+  struct fp8_write_arg wa[64];
+  int nt = num_threads < 1 ? 1 : (num_threads > 64 ? 64 : num_threads);
+  jb.num_threads = nt;
+  int started = 0;
+  for (int t = 0; t < nt; ++t) {
+    wa[t].jb = &jb;
+    wa[t].tid = t;
+    if (pthread_create(&th[t], NULL, fp8_write_worker, &wa[t]) != 0)
+      break;
+    ++started;
+  }
+  for (int t = started; t < nt; ++t) /* threads that never started */
+    fp8_write_worker(&wa[t]);
+  for (int t = 0; t < started; ++t)
+    pthread_join(th[t], NULL);
+  return OR_OK;
+}
+
+/* Element-wise encoding, exported so it can be checked on its own. */
+int oracle_e4m3_encode(const float *src, uint8_t *dst, int64_t n) {
+  if (n < 0)
+    return OR_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    dst[i] = e4m3_encode(src[i]);
   return OR_OK;
 }

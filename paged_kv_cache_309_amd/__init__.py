@@ -8,6 +8,8 @@ step runs in the HIP kernels, and an error status raises PkvError.
 Cache tensors (allocate them with new_kv_cache):
     k_cache  [num_blocks, num_kv_heads, block_size, head_dim]
     v_cache  [num_blocks, num_kv_heads, block_size // 4, head_dim, 4]
+Caches of dtype torch.float8_e4m3fn hold 8-bit E4M3 codes with one scale per
+pool (k_scale, v_scale); the calls then route to the *_fp8 entry points.
 """
 from __future__ import annotations
 
@@ -64,6 +66,10 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int,
     return k, v
 
 
+def _is_fp8(cache: torch.Tensor) -> bool:
+    return cache.dtype == torch.float8_e4m3fn
+
+
 def _dims(q: torch.Tensor, k_cache: torch.Tensor,
           block_tables: torch.Tensor) -> PkvDims:
     S, Hq, D = q.shape
@@ -73,11 +79,19 @@ def _dims(q: torch.Tensor, k_cache: torch.Tensor,
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor,
                       k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      slot_mapping: torch.Tensor, stream=None) -> None:
-    """Write k[i], v[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64)."""
+                      slot_mapping: torch.Tensor, stream=None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Write k[i], v[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64);
+    8-bit caches store the E4M3 value nearest to x / scale."""
     T, Hkv, D = k.shape
     NB, bs = k_cache.shape[0], k_cache.shape[2]
     dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k))
+    if _is_fp8(k_cache):
+        _lib.check(_lib.lib().reshape_and_cache_fp8(
+            _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+            T, bs, float(k_scale), float(v_scale), ctypes.byref(dims),
+            _stream(stream)))
+        return
     _lib.check(_lib.lib().reshape_and_cache(
         _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         T, bs, ctypes.byref(dims), _stream(stream)))
@@ -88,11 +102,19 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor,
                            block_tables: torch.Tensor,
                            context_lens: torch.Tensor, scale: float,
                            block_size: int | None = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, k_scale: float = 1.0,
+                           v_scale: float = 1.0) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K) V over context_lens[s]
     tokens reached through block_tables[s]; single launch."""
     bs = block_size or k_cache.shape[2]
     dims = _dims(q, k_cache, block_tables)
+    if _is_fp8(k_cache):
+        _lib.check(_lib.lib().paged_attention_decode_fp8(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), _ptr(context_lens), float(scale), bs,
+            float(k_scale), float(v_scale), ctypes.byref(dims),
+            _stream(stream)))
+        return out
     _lib.check(_lib.lib().paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), bs, ctypes.byref(dims),
@@ -118,12 +140,21 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
                                  partition_size: int,
                                  workspace: torch.Tensor,
                                  block_size: int | None = None,
-                                 stream=None) -> torch.Tensor:
+                                 stream=None, k_scale: float = 1.0,
+                                 v_scale: float = 1.0) -> torch.Tensor:
     """Same result as paged_attention_decode, in two launches: per-partition
     partials into `workspace` (a device byte tensor of at least
     split_workspace_bytes(...)), then the partition reduce."""
     bs = block_size or k_cache.shape[2]
     dims = _dims(q, k_cache, block_tables)
+    if _is_fp8(k_cache):
+        _lib.check(_lib.lib().paged_attention_decode_split_fp8(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), _ptr(context_lens), float(scale), bs,
+            int(partition_size), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), float(k_scale),
+            float(v_scale), ctypes.byref(dims), _stream(stream)))
+        return out
     _lib.check(_lib.lib().paged_attention_decode_split(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), bs, int(partition_size),
@@ -137,7 +168,8 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Copy-on-write: block block_mapping[i, 1] of both caches becomes a
     copy of block block_mapping[i, 0] (device int64 [n, 2])."""
     NB, Hkv, bs, D = k_cache.shape
-    dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k_cache))
+    dt = _lib.PKV_E4M3 if _is_fp8(k_cache) else _dtype(k_cache)
+    dims = PkvDims(0, Hkv, Hkv, D, NB, 0, dt)
     n = block_mapping.shape[0] if block_mapping.numel() else 0
     _lib.check(_lib.lib().copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if n else None, n,

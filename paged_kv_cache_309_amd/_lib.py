@@ -10,7 +10,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_E4M3 = 0, 1, 2, 3
 
 STATUS = {
     0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DTYPE",
@@ -18,13 +18,15 @@ STATUS = {
     6: "PKV_ERR_SHAPE", 7: "PKV_ERR_ALIGN", 8: "PKV_ERR_PARTITION",
     9: "PKV_ERR_WORKSPACE", 10: "PKV_ERR_LAUNCH", 11: "PKV_ERR_ALIAS",
     12: "PKV_ERR_NO_BLOCKS", 13: "PKV_ERR_UNKNOWN_SEQ",
-    14: "PKV_ERR_SEQ_EXISTS", 15: "PKV_ERR_CAPACITY",
+    14: "PKV_ERR_SEQ_EXISTS", 15: "PKV_ERR_CAPACITY", 16: "PKV_ERR_SCALE",
 }
 
 # every function include/*.h declares
 EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "paged_attention_split_workspace_bytes",
            "paged_attention_decode_split", "pkv_status_string", "pkv_version",
+           "reshape_and_cache_fp8", "paged_attention_decode_fp8",
+           "paged_attention_decode_split_fp8",
            "copy_blocks", "pkv_bm_create", "pkv_bm_destroy",
            "pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_tokens",
            "pkv_bm_free_sequence", "pkv_bm_batch_tables",
@@ -64,6 +66,14 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_split.restype = I
     lib.paged_attention_decode_split.argtypes = [P, P, P, P, P, P, F, I, I, P,
                                                  ctypes.c_size_t, D, P]
+    lib.reshape_and_cache_fp8.restype = I
+    lib.reshape_and_cache_fp8.argtypes = [P, P, P, P, P, I, I, F, F, D, P]
+    lib.paged_attention_decode_fp8.restype = I
+    lib.paged_attention_decode_fp8.argtypes = [P, P, P, P, P, P, F, I, F, F, D,
+                                               P]
+    lib.paged_attention_decode_split_fp8.restype = I
+    lib.paged_attention_decode_split_fp8.argtypes = [
+        P, P, P, P, P, P, F, I, I, P, ctypes.c_size_t, F, F, D, P]
     lib.copy_blocks.restype = I
     lib.copy_blocks.argtypes = [P, P, P, I, I, D, P]
     I32, I64 = ctypes.c_int32, ctypes.c_int64

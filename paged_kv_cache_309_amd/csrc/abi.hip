@@ -17,7 +17,11 @@ constexpr int kMaxGridYZ = 65535;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_E4M3 ? 1 : 2); }
+
+constexpr int kCacheSame = -1;  // the caches hold dims->dtype
+
+bool scale_ok(float x) { return x > 0.f && x <= 3.0e38f; }  // finite, positive
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   if (na == 0 || nb == 0) return false;
@@ -26,8 +30,9 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 // Checks shared by the decode entry points; fills the byte sizes.
+// cache_elem: bytes of one cache element (dtype's size, or 1 for E4M3).
 int check_decode(const pkv_dims *d, int block_size, size_t *q_bytes,
-                 size_t *cache_bytes) {
+                 size_t *cache_bytes, int cache_elem = 0) {
   if (!d) return PKV_ERR_NULL;
   if (d->dtype < PKV_F32 || d->dtype > PKV_BF16) return PKV_ERR_DTYPE;
   if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
@@ -40,8 +45,9 @@ int check_decode(const pkv_dims *d, int block_size, size_t *q_bytes,
   if ((int64_t)d->max_blocks_per_seq * block_size > INT_MAX / 2) return PKV_ERR_SHAPE;
   const u128 e = (u128)elem_bytes(d->dtype);
   const u128 qb = (u128)d->num_seqs * (u128)d->num_heads * (u128)d->head_dim * e;
+  const u128 ce = cache_elem ? (u128)cache_elem : e;
   const u128 cb = (u128)d->num_blocks * (u128)d->num_kv_heads * (u128)block_size *
-                  (u128)d->head_dim * e;
+                  (u128)d->head_dim * ce;
   if (qb > ((u128)1 << 62) || cb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
   *q_bytes = (size_t)qb;
   *cache_bytes = (size_t)cb;
@@ -69,7 +75,8 @@ int check_decode_ptrs(void *out, const void *q, const void *k_cache,
 pkv::DecodeArgs make_args(void *out, const void *q, const void *k_cache,
                           const void *v_cache, const int32_t *block_tables,
                           const int32_t *context_lens, float scale,
-                          int block_size, const pkv_dims *d) {
+                          int block_size, const pkv_dims *d,
+                          float k_scale = 1.f, float v_scale = 1.f) {
   pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -77,8 +84,10 @@ pkv::DecodeArgs make_args(void *out, const void *q, const void *k_cache,
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  // the softmax runs in base 2: exp(x * scale) = 2^(x * scale * log2 e)
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  // the softmax runs in base 2: exp(x * scale) = 2^(x * scale * log2 e); an
+  // 8-bit cache's key scale multiplies every logit and is folded in too
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634074);
+  a.v_scale = v_scale;
   a.num_seqs = d->num_seqs;
   a.num_heads = d->num_heads;
   a.num_kv_heads = d->num_kv_heads;
@@ -118,22 +127,24 @@ int split_ws_bytes(const pkv_dims *d, int block_size, int partition_size,
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int reshape_and_cache(const void *k, const void *v, void *k_cache,
-                      void *v_cache, const int64_t *slot_mapping,
-                      int num_tokens, int block_size, const pkv_dims *dims,
-                      pkv_stream_t stream) {
+int cache_write(const void *k, const void *v, void *k_cache, void *v_cache,
+                const int64_t *slot_mapping, int num_tokens, int block_size,
+                const pkv_dims *dims, pkv_stream_t stream, int cache_dtype,
+                float k_scale, float v_scale) {
   if (!dims) return PKV_ERR_NULL;
   if (dims->dtype < PKV_F32 || dims->dtype > PKV_BF16) return PKV_ERR_DTYPE;
   if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
   if (dims->head_dim != 64 && dims->head_dim != 128) return PKV_ERR_HEAD_DIM;
   if (dims->num_kv_heads <= 0) return PKV_ERR_HEADS;
   if (num_tokens < 0 || dims->num_blocks < 0) return PKV_ERR_SHAPE;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
   const u128 e = (u128)elem_bytes(dims->dtype);
+  const u128 ce = cache_dtype == kCacheSame ? e : 1;
   const u128 tb = (u128)num_tokens * (u128)dims->num_kv_heads * (u128)dims->head_dim * e;
   const u128 cb = (u128)dims->num_blocks * (u128)dims->num_kv_heads * (u128)block_size *
-                  (u128)dims->head_dim * e;
+                  (u128)dims->head_dim * ce;
   if (tb > ((u128)1 << 62) || cb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
@@ -153,9 +164,102 @@ int reshape_and_cache(const void *k, const void *v, void *k_cache,
   a.num_tokens = num_tokens;
   a.num_kv_heads = dims->num_kv_heads;
   a.num_blocks = dims->num_blocks;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
   const hipError_t err = pkv::launch_reshape_and_cache(
-      a, dims->dtype, dims->head_dim, block_size, reinterpret_cast<hipStream_t>(stream));
+      a, dims->dtype, ct, dims->head_dim, block_size, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+           const int32_t *block_tables, const int32_t *context_lens, float scale,
+           int block_size, const pkv_dims *dims, pkv_stream_t stream,
+           int cache_dtype, float k_scale, float v_scale) {
+  size_t qb = 0, cb = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb, cache_dtype == kCacheSame ? 0 : 1);
+  if (rc != PKV_OK) return rc;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
+  if (cache_dtype != kCacheSame && dims->dtype == PKV_F32 && use_mfma(dims))
+    return PKV_ERR_DTYPE;
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  const pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
+                                      context_lens, scale, block_size, dims, k_scale,
+                                      v_scale);
+  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t err =
+      use_mfma(dims)
+          ? pkv::launch_decode_mfma(a, dims->dtype, ct, dims->head_dim, block_size, false, st)
+          : pkv::launch_decode_vector(a, dims->dtype, ct, dims->head_dim, block_size, false, st);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int decode_split(void *out, const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 int block_size, int partition_size, void *workspace,
+                 size_t workspace_bytes, const pkv_dims *dims, pkv_stream_t stream,
+                 int cache_dtype, float k_scale, float v_scale) {
+  size_t qb = 0, cb = 0, need = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb, cache_dtype == kCacheSame ? 0 : 1);
+  if (rc != PKV_OK) return rc;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
+  if (cache_dtype != kCacheSame && dims->dtype == PKV_F32 && use_mfma(dims))
+    return PKV_ERR_DTYPE;
+  rc = split_ws_bytes(dims, block_size, partition_size, &need);
+  if (rc != PKV_OK) return rc;
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb) ||
+      overlap(workspace, need, k_cache, cb) || overlap(workspace, need, v_cache, cb))
+    return PKV_ERR_ALIAS;
+
+  pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
+                                context_lens, scale, block_size, dims, k_scale, v_scale);
+  const int P = num_partitions(dims, block_size, partition_size);
+  a.num_parts = P > 0 ? P : 1;  // P == 0: no token can be attended; the reduce writes zeros
+  a.part_tokens = partition_size;
+  const size_t n = (size_t)dims->num_seqs * dims->num_heads * a.num_parts;
+  a.ws_o = static_cast<float *>(workspace);
+  a.ws_m = a.ws_o + n * dims->head_dim;
+  a.ws_l = a.ws_m + n;
+
+  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (P > 0) {
+    err = use_mfma(dims)
+              ? pkv::launch_decode_mfma(a, dims->dtype, ct, dims->head_dim, block_size, true, st)
+              : pkv::launch_decode_vector(a, dims->dtype, ct, dims->head_dim, block_size, true, st);
+  }
+  if (err == hipSuccess) err = pkv::launch_partition_reduce(a, dims->dtype, dims->head_dim, st);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int reshape_and_cache(const void *k, const void *v, void *k_cache,
+                      void *v_cache, const int64_t *slot_mapping,
+                      int num_tokens, int block_size, const pkv_dims *dims,
+                      pkv_stream_t stream) {
+  return cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, block_size, dims,
+                     stream, kCacheSame, 1.f, 1.f);
+}
+
+int reshape_and_cache_fp8(const void *k, const void *v, void *k_cache,
+                          void *v_cache, const int64_t *slot_mapping,
+                          int num_tokens, int block_size, float k_scale,
+                          float v_scale, const pkv_dims *dims,
+                          pkv_stream_t stream) {
+  return cache_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, block_size, dims,
+                     stream, pkv::DT_FP8, k_scale, v_scale);
 }
 
 int paged_attention_decode(void *out, const void *q, const void *k_cache,
@@ -163,20 +267,17 @@ int paged_attention_decode(void *out, const void *q, const void *k_cache,
                            const int32_t *context_lens, float scale,
                            int block_size, const pkv_dims *dims,
                            pkv_stream_t stream) {
-  size_t qb = 0, cb = 0;
-  int rc = check_decode(dims, block_size, &qb, &cb);
-  if (rc != PKV_OK) return rc;
-  if (dims->num_seqs == 0) return PKV_OK;
-  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
-  if (rc != PKV_OK) return rc;
-  const pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
-                                      context_lens, scale, block_size, dims);
-  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t err =
-      use_mfma(dims)
-          ? pkv::launch_decode_mfma(a, dims->dtype, dims->head_dim, block_size, false, st)
-          : pkv::launch_decode_vector(a, dims->dtype, dims->head_dim, block_size, false, st);
-  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  return decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                dims, stream, kCacheSame, 1.f, 1.f);
+}
+
+int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, float scale,
+                               int block_size, float k_scale, float v_scale,
+                               const pkv_dims *dims, pkv_stream_t stream) {
+  return decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                dims, stream, pkv::DT_FP8, k_scale, v_scale);
 }
 
 int paged_attention_split_workspace_bytes(const pkv_dims *dims, int block_size,
@@ -195,50 +296,29 @@ int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
                                  int block_size, int partition_size,
                                  void *workspace, size_t workspace_bytes,
                                  const pkv_dims *dims, pkv_stream_t stream) {
-  size_t qb = 0, cb = 0, need = 0;
-  int rc = check_decode(dims, block_size, &qb, &cb);
-  if (rc != PKV_OK) return rc;
-  rc = split_ws_bytes(dims, block_size, partition_size, &need);
-  if (rc != PKV_OK) return rc;
-  if (dims->num_seqs == 0) return PKV_OK;
-  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
-  if (rc != PKV_OK) return rc;
-  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-  if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb) ||
-      overlap(workspace, need, k_cache, cb) || overlap(workspace, need, v_cache, cb))
-    return PKV_ERR_ALIAS;
+  return decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      block_size, partition_size, workspace, workspace_bytes, dims, stream,
+                      kCacheSame, 1.f, 1.f);
+}
 
-  pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,
-                                context_lens, scale, block_size, dims);
-  const int P = num_partitions(dims, block_size, partition_size);
-  if (P == 0) {  // no token can be attended: the reduce writes zeros
-    a.num_parts = 1;
-  } else {
-    a.num_parts = P;
-  }
-  a.part_tokens = partition_size;
-  const size_t n = (size_t)dims->num_seqs * dims->num_heads * a.num_parts;
-  a.ws_o = static_cast<float *>(workspace);
-  a.ws_m = a.ws_o + n * dims->head_dim;
-  a.ws_l = a.ws_m + n;
-
-  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t err = hipSuccess;
-  if (P > 0) {
-    err = use_mfma(dims)
-              ? pkv::launch_decode_mfma(a, dims->dtype, dims->head_dim, block_size, true, st)
-              : pkv::launch_decode_vector(a, dims->dtype, dims->head_dim, block_size, true, st);
-  }
-  if (err == hipSuccess) err = pkv::launch_partition_reduce(a, dims->dtype, dims->head_dim, st);
-  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+int paged_attention_decode_split_fp8(void *out, const void *q, const void *k_cache,
+                                     const void *v_cache,
+                                     const int32_t *block_tables,
+                                     const int32_t *context_lens, float scale,
+                                     int block_size, int partition_size,
+                                     void *workspace, size_t workspace_bytes,
+                                     float k_scale, float v_scale,
+                                     const pkv_dims *dims, pkv_stream_t stream) {
+  return decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      block_size, partition_size, workspace, workspace_bytes, dims, stream,
+                      pkv::DT_FP8, k_scale, v_scale);
 }
 
 int copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
                 int num_pairs, int block_size, const pkv_dims *dims,
                 pkv_stream_t stream) {
   if (!dims) return PKV_ERR_NULL;
-  if (dims->dtype < PKV_F32 || dims->dtype > PKV_BF16) return PKV_ERR_DTYPE;
+  if (dims->dtype < PKV_F32 || dims->dtype > PKV_E4M3) return PKV_ERR_DTYPE;
   if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
   if (dims->head_dim != 64 && dims->head_dim != 128) return PKV_ERR_HEAD_DIM;
   if (dims->num_kv_heads <= 0) return PKV_ERR_HEADS;
@@ -284,6 +364,7 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence id";
     case PKV_ERR_SEQ_EXISTS: return "sequence id already in use";
     case PKV_ERR_CAPACITY: return "output buffer too small";
+    case PKV_ERR_SCALE: return "a dequantisation scale is not a finite positive number";
     default: return "unknown status";
   }
 }

@@ -80,20 +80,42 @@ template <> struct MfmaOps<DT_F16> {
   }
 };
 
-template <int D>
+// One 16-token tile as loaded: 16-byte chunks of K and of V per lane.
+// 16-bit caches: chunk kk of K is the A operand of logit MFMA kk, chunk u of
+// V holds the A operands of value n-tiles 2u and 2u+1.  8-bit caches: chunk
+// cp of K holds logit MFMAs 2cp and 2cp+1, chunk u of V holds n-tiles
+// 4u .. 4u+3; they are widened to 16 bits in registers.
+template <int CT, int D>
 struct MfmaTile {
-  u32x4 k[D / 32];  // A operands of the logit products
-  u32x4 v[D / 32];  // A operands of two value products each
+  static constexpr int NC = CT == DT_FP8 ? D / 64 : D / 32;
+  u32x4 k[NC];
+  u32x4 v[NC];
 };
 
-template <int DT, int D, int BS, bool SPLIT>
+// Two E4M3 bytes -> two 16-bit operands of type OT, exactly (every E4M3
+// value is a bfloat16 and a binary16 value).
+template <int OT>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w, bool hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
+                     : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  if constexpr (OT == DT_BF16) {
+    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+  }
+}
+
+// QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
+template <int QT, int CT, int D, int BS, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_mfma_kernel(DecodeArgs a) {
-  using Ops = MfmaOps<DT>;
-  using Tl = MfmaTile<D>;
-  constexpr int E = 2;
-  constexpr int KC = D / 32;   // logit MFMAs and V chunks per tile
-  constexpr int NT = D / 16;   // value n-tiles
+  using Ops = MfmaOps<QT>;
+  using Tl = MfmaTile<CT, D>;
+  constexpr bool F8 = CT == DT_FP8;
+  constexpr int E = Elem<CT>::bytes;  // cache element bytes
+  constexpr int KC = D / 32;          // logit MFMAs per tile
+  constexpr int NT = D / 16;          // value n-tiles
 
   const int g = blockIdx.x, part = blockIdx.z;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
@@ -120,19 +142,23 @@ decode_mfma_kernel(DecodeArgs a) {
   if (tok_begin >= tok_end) {
     if (!SPLIT) {
       for (int i = tid; i < G * D; i += kDecodeThreads)
-        store_elem<DT>(a.out, ((size_t)s * Hq + g * G) * D + i, 0.f);
+        store_elem<QT>(a.out, ((size_t)s * Hq + g * G) * D + i, 0.f);
     }
     return;
   }
 
-  // Q^T operand: lane holds head `col`, dims (kk*4+grp)*8 .. +8
+  // Q^T operand: lane holds head `col` and the eight dims the K operand of
+  // logit MFMA kk holds in this lane: (kk*4+grp)*8 for 16-bit caches,
+  // (kk/2)*64 + grp*16 + (kk%2)*8 for 8-bit caches
   u32x4 qop[KC];
   {
-    const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * E;
+    const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * 2;
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-      qop[kk] = col < G ? *reinterpret_cast<const u32x4 *>(qp + (kk * 4 + grp) * 16)
+    for (int kk = 0; kk < KC; ++kk) {
+      const int d0 = F8 ? (kk / 2) * 64 + grp * 16 + (kk % 2) * 8 : (kk * 4 + grp) * 8;
+      qop[kk] = col < G ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
                         : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   const char *kc = static_cast<const char *>(a.k_cache);
@@ -144,9 +170,10 @@ decode_mfma_kernel(DecodeArgs a) {
   const int n_tiles = st_end - st_begin;
   const int n_mine = n_tiles > w ? (n_tiles - w + 3) >> 2 : 0;
 
-  // lane offsets inside a tile, in bytes
-  const uint32_t koff = (uint32_t)(col * D * E + grp * 16);         // + kk*64
-  const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);     // + u*256
+  // lane offsets inside a tile, in bytes (chunk c adds c*64 for K, c*256
+  // for V): K row `col`, V token group `grp`
+  const uint32_t koff = (uint32_t)(col * D * E + grp * 16);
+  const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);
 
   float m = -INFINITY, l = 0.f;  // head `col`; l is this lane's share
   f32x4 acc[NT];
@@ -157,16 +184,26 @@ decode_mfma_kernel(DecodeArgs a) {
     const char *kp = kc + tile_bytes + koff;
     const char *vp = vc + tile_bytes + voff;
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) t.k[kk] = load_stream16(kp + kk * 64);
+    for (int c = 0; c < Tl::NC; ++c) t.k[c] = load_stream16(kp + c * 64);
 #pragma unroll
-    for (int u = 0; u < KC; ++u) t.v[u] = load_stream16(vp + u * 256);
+    for (int c = 0; c < Tl::NC; ++c) t.v[c] = load_stream16(vp + c * 256);
   };
 
   auto compute = [&](Tl &t, int n) {
     // S^T[token 4*grp+i][head col]
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F8) {
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[kk], sacc);
+      for (int kk = 0; kk < KC; ++kk) {
+        const uint32_t w0 = t.k[kk / 2][2 * (kk % 2)], w1 = t.k[kk / 2][2 * (kk % 2) + 1];
+        const u32x4 kop = {fp8x2_to_16<QT>(w0, false), fp8x2_to_16<QT>(w0, true),
+                           fp8x2_to_16<QT>(w1, false), fp8x2_to_16<QT>(w1, true)};
+        sacc = Ops::qk(kop, qop[kk], sacc);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[kk], sacc);
+    }
 
     const int t0 = (st_begin + w + 4 * n) * 16 + 4 * grp;
     const bool tail = (st_begin + w + 4 * n) * 16 + 16 > tok_end;
@@ -177,14 +214,25 @@ decode_mfma_kernel(DecodeArgs a) {
       sc[i] = (i < nvalid && col < G) ? sacc[i] * a.scale_log2 : -INFINITY;
     if (tail) {
       // masked tokens' values may hold anything (NaN included): zero them
-      const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-      const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+      if constexpr (F8) {
+        const uint32_t mk = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
 #pragma unroll
-      for (int u = 0; u < KC; ++u) {
-        t.v[u][0] &= m01;
-        t.v[u][1] &= m23;
-        t.v[u][2] &= m01;
-        t.v[u][3] &= m23;
+        for (int c = 0; c < Tl::NC; ++c) {
+          t.v[c][0] &= mk;
+          t.v[c][1] &= mk;
+          t.v[c][2] &= mk;
+          t.v[c][3] &= mk;
+        }
+      } else {
+        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int c = 0; c < Tl::NC; ++c) {
+          t.v[c][0] &= m01;
+          t.v[c][1] &= m23;
+          t.v[c][2] &= m01;
+          t.v[c][3] &= m23;
+        }
       }
     }
 
@@ -213,13 +261,27 @@ decode_mfma_kernel(DecodeArgs a) {
     Ops::split2(p[2], p[3], h23, l23);
     const u32x2 phi = {h01, h23};
     const u32x2 plo = {l01, l23};
+    if constexpr (F8) {
+      // chunk u, word j: the four tokens of dim 64u + 4*col + j -> n-tile 4u+j
 #pragma unroll
-    for (int u = 0; u < KC; ++u) {
+      for (int u = 0; u < Tl::NC; ++u) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
-        acc[2 * u + j] = Ops::pv(va, phi, acc[2 * u + j]);
-        acc[2 * u + j] = Ops::pv(va, plo, acc[2 * u + j]);
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 va = {fp8x2_to_16<QT>(t.v[u][j], false), fp8x2_to_16<QT>(t.v[u][j], true)};
+          acc[4 * u + j] = Ops::pv(va, phi, acc[4 * u + j]);
+          acc[4 * u + j] = Ops::pv(va, plo, acc[4 * u + j]);
+        }
+      }
+    } else {
+      // chunk u, words 2j..2j+1: the four tokens of dim 32u + 2*col + j
+#pragma unroll
+      for (int u = 0; u < Tl::NC; ++u) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
+          acc[2 * u + j] = Ops::pv(va, phi, acc[2 * u + j]);
+          acc[2 * u + j] = Ops::pv(va, plo, acc[2 * u + j]);
+        }
       }
     }
   };
@@ -232,14 +294,16 @@ decode_mfma_kernel(DecodeArgs a) {
   // ---- merge the 4 wavefronts through LDS ----
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  // acc[2u+j][i] is dim 32u + 2(4*grp+i) + j of head col
+  // n-tile row m = 4*grp + i of head col is dim 32u + 2m + j (n-tile
+  // 2u+j, 16-bit caches) or 64u + 4m + j (n-tile 4u+j, 8-bit caches)
 #pragma unroll
-  for (int u = 0; u < KC; ++u)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm_o[w][col][32 * u + 2 * (4 * grp + i) + j] = acc[2 * u + j][i];
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * grp + i;
+      const int d = F8 ? 64 * (nt / 4) + 4 * m + nt % 4 : 32 * (nt / 2) + 2 * m + nt % 2;
+      sm_o[w][col][d] = acc[nt][i];
+    }
   if (grp == 0) {
     sm_m[w][col] = m;
     sm_l[w][col] = lt;
@@ -258,6 +322,7 @@ decode_mfma_kernel(DecodeArgs a) {
       den = fmaf(f, sm_l[i][hh], den);
     }
     const int h = g * G + hh;
+    num *= a.v_scale;  // value dequantisation (1 for 16-bit caches)
     if constexpr (SPLIT) {
       const size_t pi = ((size_t)s * Hq + h) * a.num_parts + part;
       a.ws_o[pi * D + d] = num;
@@ -266,37 +331,42 @@ decode_mfma_kernel(DecodeArgs a) {
         a.ws_l[pi] = den;
       }
     } else {
-      store_elem<DT>(a.out, ((size_t)s * Hq + h) * D + d, num / den);
+      store_elem<QT>(a.out, ((size_t)s * Hq + h) * D + d, num / den);
     }
   }
 }
 
-template <int DT, int D, int BS>
+template <int QT, int CT, int D, int BS>
 static hipError_t launch_mfma(const DecodeArgs &a, bool split, hipStream_t st) {
   dim3 grid(a.num_kv_heads, a.num_seqs, split ? a.num_parts : 1);
   if (split)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, BS, true>), grid,
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, true>), grid,
                        dim3(kDecodeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, BS, false>), grid,
+    hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, false>), grid,
                        dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int QT, int CT>
 static hipError_t launch_mfma_dt(const DecodeArgs &a, int head_dim,
                                  int block_size, bool split, hipStream_t st) {
   if (head_dim == 128)
-    return block_size == 16 ? launch_mfma<DT, 128, 16>(a, split, st)
-                            : launch_mfma<DT, 128, 32>(a, split, st);
-  return block_size == 16 ? launch_mfma<DT, 64, 16>(a, split, st)
-                          : launch_mfma<DT, 64, 32>(a, split, st);
+    return block_size == 16 ? launch_mfma<QT, CT, 128, 16>(a, split, st)
+                            : launch_mfma<QT, CT, 128, 32>(a, split, st);
+  return block_size == 16 ? launch_mfma<QT, CT, 64, 16>(a, split, st)
+                          : launch_mfma<QT, CT, 64, 32>(a, split, st);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int head_dim,
-                              int block_size, bool split, hipStream_t st) {
-  if (dtype == DT_F16) return launch_mfma_dt<DT_F16>(a, head_dim, block_size, split, st);
-  return launch_mfma_dt<DT_BF16>(a, head_dim, block_size, split, st);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int cache_dtype,
+                              int head_dim, int block_size, bool split,
+                              hipStream_t st) {
+  if (cache_dtype == DT_FP8) {
+    if (dtype == DT_F16) return launch_mfma_dt<DT_F16, DT_FP8>(a, head_dim, block_size, split, st);
+    return launch_mfma_dt<DT_BF16, DT_FP8>(a, head_dim, block_size, split, st);
+  }
+  if (dtype == DT_F16) return launch_mfma_dt<DT_F16, DT_F16>(a, head_dim, block_size, split, st);
+  return launch_mfma_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, split, st);
 }
 
 }  // namespace pkv

@@ -49,11 +49,13 @@ struct VecTile {
   uint32_t v[VW];
 };
 
-template <int DT, int D, int BS, bool SPLIT>
+// QT: element type of q and out; CT: of the caches (QT, or 8-bit E4M3)
+template <int QT, int CT, int D, int BS, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_vector_kernel(DecodeArgs a) {
-  using Tl = VecTile<DT, D>;
+  using Tl = VecTile<CT, D>;
   constexpr int E = Tl::E;
+  constexpr int KWQ = Tl::DQ * Elem<QT>::bytes / 4;  // words of q per lane
   constexpr int NACC = Tl::VI * Tl::DPV;  // == D / 16
 
   const int h = blockIdx.x, part = blockIdx.z;
@@ -81,20 +83,21 @@ decode_vector_kernel(DecodeArgs a) {
 
   if (tok_begin >= tok_end) {
     if (!SPLIT) {
-      for (int d = tid; d < D; d += kDecodeThreads) store_elem<DT>(a.out, orow + d, 0.f);
+      for (int d = tid; d < D; d += kDecodeThreads) store_elem<QT>(a.out, orow + d, 0.f);
     }
     return;  // an empty partition leaves its workspace entry unused
   }
 
-  // q for this lane's dims, pre-multiplied by scale * log2(e)
+  // q for this lane's dims, pre-multiplied by scale * log2(e) (and the
+  // key dequantisation scale of an 8-bit cache)
   float qv[Tl::DQ];
   {
-    uint32_t qw[Tl::KW];
-    const char *qp = static_cast<const char *>(a.q) + (orow + c * Tl::DQ) * E;
+    uint32_t qw[KWQ];
+    const char *qp = static_cast<const char *>(a.q) + (orow + c * Tl::DQ) * Elem<QT>::bytes;
 #pragma unroll
-    for (int u = 0; u < Tl::KW; ++u) qw[u] = reinterpret_cast<const uint32_t *>(qp)[u];
+    for (int u = 0; u < KWQ; ++u) qw[u] = reinterpret_cast<const uint32_t *>(qp)[u];
 #pragma unroll
-    for (int e = 0; e < Tl::DQ; ++e) qv[e] = elem<DT>(qw, e) * a.scale_log2;
+    for (int e = 0; e < Tl::DQ; ++e) qv[e] = elem<QT>(qw, e) * a.scale_log2;
   }
 
   const char *kc = static_cast<const char *>(a.k_cache);
@@ -120,7 +123,9 @@ decode_vector_kernel(DecodeArgs a) {
     const char *vp = vc + tile_bytes + voff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (Tl::KW == 2) {
+      if constexpr (Tl::KW == 1) {
+        t.k[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(kp + i * D * E));
+      } else if constexpr (Tl::KW == 2) {
         const u32x2 x = load_stream8(kp + i * D * E);
         t.k[i][0] = x[0];
         t.k[i][1] = x[1];
@@ -152,7 +157,7 @@ decode_vector_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < Tl::DQ; ++e) d = fmaf(qv[e], elem<DT>(t.k[i], e), d);
+      for (int e = 0; e < Tl::DQ; ++e) d = fmaf(qv[e], elem<CT>(t.k[i], e), d);
       sc[i] = row_sum16(d);
     }
     const int tile_tok = (st_begin + w + 4 * n) * 16;
@@ -163,7 +168,12 @@ decode_vector_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i >= nvalid) sc[i] = -INFINITY;
-      if constexpr (E == 2) {
+      if constexpr (E == 1) {
+        // one word = one dim's four tokens, one byte each
+        const uint32_t mk = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
+#pragma unroll
+        for (int u = 0; u < Tl::VW; ++u) t.v[u] &= mk;
+      } else if constexpr (E == 2) {
         const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
         const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
@@ -200,12 +210,13 @@ decode_vector_kernel(DecodeArgs a) {
     for (int ii = 0; ii < Tl::VI; ++ii) {
 #pragma unroll
       for (int k2 = 0; k2 < Tl::DPV; ++k2) {
-        const uint32_t *wv = &t.v[4 * ii + (E == 2 ? 2 * k2 : 0)];
+        // the four tokens of one dim: k2*E words into the 16-byte chunk
+        const uint32_t *wv = &t.v[4 * ii + k2 * E];
         float x = acc[ii * Tl::DPV + k2];
-        x = fmaf(p[0], elem<DT>(wv, 0), x);
-        x = fmaf(p[1], elem<DT>(wv, 1), x);
-        x = fmaf(p[2], elem<DT>(wv, 2), x);
-        x = fmaf(p[3], elem<DT>(wv, 3), x);
+        x = fmaf(p[0], elem<CT>(wv, 0), x);
+        x = fmaf(p[1], elem<CT>(wv, 1), x);
+        x = fmaf(p[2], elem<CT>(wv, 2), x);
+        x = fmaf(p[3], elem<CT>(wv, 3), x);
         acc[ii * Tl::DPV + k2] = x;
       }
     }
@@ -241,6 +252,7 @@ decode_vector_kernel(DecodeArgs a) {
       num = fmaf(f, sm_acc[i][d], num);
       den = fmaf(f, sm_l[i], den);
     }
+    num *= a.v_scale;  // value dequantisation (1 for 16/32-bit caches)
     if constexpr (SPLIT) {
       const size_t pi = ((size_t)s * Hq + h) * a.num_parts + part;
       a.ws_o[pi * D + d] = num;
@@ -249,39 +261,47 @@ decode_vector_kernel(DecodeArgs a) {
         a.ws_l[pi] = den;
       }
     } else {
-      store_elem<DT>(a.out, orow + d, num / den);
+      store_elem<QT>(a.out, orow + d, num / den);
     }
   }
 }
 
-template <int DT, int D, int BS>
+template <int QT, int CT, int D, int BS>
 static hipError_t launch_vec(const DecodeArgs &a, bool split, hipStream_t st) {
   dim3 grid(a.num_heads, a.num_seqs, split ? a.num_parts : 1);
   if (split)
-    hipLaunchKernelGGL((decode_vector_kernel<DT, D, BS, true>), grid,
+    hipLaunchKernelGGL((decode_vector_kernel<QT, CT, D, BS, true>), grid,
                        dim3(kDecodeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_vector_kernel<DT, D, BS, false>), grid,
+    hipLaunchKernelGGL((decode_vector_kernel<QT, CT, D, BS, false>), grid,
                        dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int QT, int CT>
 static hipError_t launch_vec_dt(const DecodeArgs &a, int head_dim,
                                 int block_size, bool split, hipStream_t st) {
   if (head_dim == 128)
-    return block_size == 16 ? launch_vec<DT, 128, 16>(a, split, st)
-                            : launch_vec<DT, 128, 32>(a, split, st);
-  return block_size == 16 ? launch_vec<DT, 64, 16>(a, split, st)
-                          : launch_vec<DT, 64, 32>(a, split, st);
+    return block_size == 16 ? launch_vec<QT, CT, 128, 16>(a, split, st)
+                            : launch_vec<QT, CT, 128, 32>(a, split, st);
+  return block_size == 16 ? launch_vec<QT, CT, 64, 16>(a, split, st)
+                          : launch_vec<QT, CT, 64, 32>(a, split, st);
 }
 
-hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int head_dim,
-                                int block_size, bool split, hipStream_t st) {
+hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int cache_dtype,
+                                int head_dim, int block_size, bool split,
+                                hipStream_t st) {
+  if (cache_dtype == DT_FP8) {
+    switch (dtype) {
+      case DT_F32: return launch_vec_dt<DT_F32, DT_FP8>(a, head_dim, block_size, split, st);
+      case DT_F16: return launch_vec_dt<DT_F16, DT_FP8>(a, head_dim, block_size, split, st);
+      default: return launch_vec_dt<DT_BF16, DT_FP8>(a, head_dim, block_size, split, st);
+    }
+  }
   switch (dtype) {
-    case DT_F32: return launch_vec_dt<DT_F32>(a, head_dim, block_size, split, st);
-    case DT_F16: return launch_vec_dt<DT_F16>(a, head_dim, block_size, split, st);
-    default: return launch_vec_dt<DT_BF16>(a, head_dim, block_size, split, st);
+    case DT_F32: return launch_vec_dt<DT_F32, DT_F32>(a, head_dim, block_size, split, st);
+    case DT_F16: return launch_vec_dt<DT_F16, DT_F16>(a, head_dim, block_size, split, st);
+    default: return launch_vec_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, split, st);
   }
 }
 

@@ -25,12 +25,23 @@ template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_FP8> { static constexpr int bytes = 1; };
 
 // Element j of a run of words (j counts elements, not words).
 template <int DT>
 __device__ __forceinline__ float elem(const uint32_t *w, int j) {
   if constexpr (DT == DT_F32) {
     return __uint_as_float(w[j]);
+  } else if constexpr (DT == DT_FP8) {
+    // E4M3 byte (j & 3) of word j / 4, widened exactly by the hardware (the
+    // byte select is an immediate: j is a constant after unrolling)
+    const int x = static_cast<int>(w[j >> 2]);
+    switch (j & 3) {
+      case 0: return __builtin_amdgcn_cvt_f32_fp8(x, 0);
+      case 1: return __builtin_amdgcn_cvt_f32_fp8(x, 1);
+      case 2: return __builtin_amdgcn_cvt_f32_fp8(x, 2);
+      default: return __builtin_amdgcn_cvt_f32_fp8(x, 3);
+    }
   } else if constexpr (DT == DT_BF16) {
     const uint32_t x = w[j >> 1];
     return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
@@ -53,6 +64,25 @@ template <> __device__ __forceinline__ uint32_t from_f32<DT_BF16>(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// float -> E4M3 byte (the OCP 8-bit float with 4 exponent bits, bias 7,
+// 3 fraction bits, no infinity, largest finite 448), nearest value with
+// ties to the even fraction; magnitudes of 448 and beyond saturate to +-448,
+// NaN gives 0x7f.  Normal results round the float's 23-bit fraction to 3
+// bits on its bit pattern; results below 2^-6 are multiples of 2^-9, found
+// by rounding y * 512 to the nearest even integer.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                    // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;            // >= 448 (and inf)
+  if (a < 0x3c800000u)                                  // below 2^-6
+    return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // exponent | 3 bits
+  const uint32_t code = r - (120u << 3);                       // bias 127 -> 7
+  return sign | (code < 0x7eu ? code : 0x7eu);
 }
 
 template <int DT>

@@ -8,7 +8,7 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 
 // Threads per workgroup of the decode kernels: four wave64 wavefronts.
 constexpr int kDecodeThreads = 256;
@@ -24,7 +24,8 @@ struct DecodeArgs {
   const void *v_cache;    // [NB, Hkv, bs/4, D, 4]
   const int32_t *block_tables;  // [S, max_blocks]
   const int32_t *context_lens;  // [S]
-  float scale_log2;       // softmax scale times log2(e)
+  float scale_log2;       // softmax scale times log2(e) times the key scale
+  float v_scale;          // value dequantisation scale (1 for 16/32-bit caches)
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -44,6 +45,8 @@ struct CacheWriteArgs {
   int64_t num_tokens;
   int num_kv_heads;
   int num_blocks;
+  float k_scale;          // 8-bit caches: stored = encode(x / scale)
+  float v_scale;
 };
 
 struct CopyBlocksArgs {
@@ -55,15 +58,18 @@ struct CopyBlocksArgs {
 };
 
 // Each returns the launch error (hipSuccess when enqueued).
-hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int head_dim,
-                                int block_size, bool split, hipStream_t st);
-hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int head_dim,
-                              int block_size, bool split, hipStream_t st);
+// dtype: of q and out; cache_dtype: of the two pools (dtype, or DT_FP8)
+hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int cache_dtype,
+                                int head_dim, int block_size, bool split,
+                                hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int cache_dtype,
+                              int head_dim, int block_size, bool split,
+                              hipStream_t st);
 hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
                                    int head_dim, hipStream_t st);
 hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
-                                    int head_dim, int block_size,
-                                    hipStream_t st);
+                                    int cache_dtype, int head_dim,
+                                    int block_size, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, int num_pairs,
                               hipStream_t st);
 

@@ -111,21 +111,90 @@ static hipError_t launch_rac_d(const CacheWriteArgs &a, int block_size, hipStrea
   return hipGetLastError();
 }
 
-template <int DT>
+// Cache write into 8-bit E4M3 pools ("PagedAttention: how vLLM manages the
+// KV cache", section "Keep the tensor formula beside the allocator model":
+// lower-precision cache formats reduce the bytes per element).  Every
+// element x is stored as e4m3(x / scale), the quotient computed in IEEE
+// single precision.  One thread converts eight consecutive dims of one
+// (token, KV head) row: one 8-byte K store, eight V bytes four apart.
+template <int IT, int D, int BS>
+__global__ void __launch_bounds__(256) reshape_and_cache_fp8_kernel(CacheWriteArgs a) {
+  constexpr int EI = Elem<IT>::bytes;
+  constexpr int CPR = D / 8;  // 8-element groups per row
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = a.num_tokens * a.num_kv_heads * CPR;
+  if (idx >= total) return;
+  const int chunk = (int)(idx % CPR);
+  const int64_t row = idx / CPR;
+  const int g = (int)(row % a.num_kv_heads);
+  const int64_t i = row / a.num_kv_heads;
+  const int64_t slot = a.slot_mapping[i];
+  if (slot < 0 || slot >= (int64_t)a.num_blocks * BS) return;
+  const int64_t p = slot / BS;
+  const int o = (int)(slot % BS);
+  const size_t src = (size_t)row * D + chunk * 8;
+  const size_t tile = ((size_t)p * a.num_kv_heads + g) * BS * D;
+
+  uint32_t kw[8 * EI / 4], vw[8 * EI / 4];
+#pragma unroll
+  for (int u = 0; u < 8 * EI / 16; ++u) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k) + src * EI + 16 * u);
+    const u32x4 y = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) + src * EI + 16 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kw[4 * u + e] = x[e];
+      vw[4 * u + e] = y[e];
+    }
+  }
+  uint32_t kq[2] = {0u, 0u};
+  uint8_t *vc = static_cast<uint8_t *>(a.v_cache);
+  const size_t vb = tile + (size_t)(o / 4) * 4 * D + (o % 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kq[e / 4] |= e4m3_from_f32(elem<IT>(kw, e) / a.k_scale) << (8 * (e % 4));
+    vc[vb + (size_t)(chunk * 8 + e) * 4] =
+        static_cast<uint8_t>(e4m3_from_f32(elem<IT>(vw, e) / a.v_scale));
+  }
+  *reinterpret_cast<u32x2 *>(static_cast<char *>(a.k_cache) + tile + (size_t)o * D + chunk * 8) =
+      u32x2{kq[0], kq[1]};
+}
+
+template <int DT, int CT>
 static hipError_t launch_rac_dt(const CacheWriteArgs &a, int head_dim, int block_size,
                                 hipStream_t st) {
-  return head_dim == 128 ? launch_rac_d<DT, 128>(a, block_size, st)
-                         : launch_rac_d<DT, 64>(a, block_size, st);
+  if constexpr (CT == DT_FP8) {
+    const int64_t total = a.num_tokens * a.num_kv_heads * (head_dim / 8);
+    const dim3 grid((unsigned)((total + 255) / 256));
+#define PKV_RAC8(DV, BV) \
+  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<DT, DV, BV>), grid, dim3(256), 0, st, a)
+    if (head_dim == 128) {
+      if (block_size == 16) PKV_RAC8(128, 16); else PKV_RAC8(128, 32);
+    } else {
+      if (block_size == 16) PKV_RAC8(64, 16); else PKV_RAC8(64, 32);
+    }
+#undef PKV_RAC8
+    return hipGetLastError();
+  } else {
+    return head_dim == 128 ? launch_rac_d<DT, 128>(a, block_size, st)
+                           : launch_rac_d<DT, 64>(a, block_size, st);
+  }
 }
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
-                                    int head_dim, int block_size,
+                                    int cache_dtype, int head_dim, int block_size,
                                     hipStream_t st) {
   if (a.num_tokens == 0) return hipSuccess;
+  if (cache_dtype == DT_FP8) {
+    switch (dtype) {
+      case DT_F32: return launch_rac_dt<DT_F32, DT_FP8>(a, head_dim, block_size, st);
+      case DT_F16: return launch_rac_dt<DT_F16, DT_FP8>(a, head_dim, block_size, st);
+      default: return launch_rac_dt<DT_BF16, DT_FP8>(a, head_dim, block_size, st);
+    }
+  }
   switch (dtype) {
-    case DT_F32: return launch_rac_dt<DT_F32>(a, head_dim, block_size, st);
-    case DT_F16: return launch_rac_dt<DT_F16>(a, head_dim, block_size, st);
-    default: return launch_rac_dt<DT_BF16>(a, head_dim, block_size, st);
+    case DT_F32: return launch_rac_dt<DT_F32, DT_F32>(a, head_dim, block_size, st);
+    case DT_F16: return launch_rac_dt<DT_F16, DT_F16>(a, head_dim, block_size, st);
+    default: return launch_rac_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, st);
   }
 }
 

@@ -141,6 +141,8 @@ def test_copy_blocks_rejects_bad_arguments():
     assert cb(d, bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
     assert cb(dims(D=32)) == ERR["PKV_ERR_HEAD_DIM"]
     assert cb(dims(dt=5)) == ERR["PKV_ERR_DTYPE"]
+    assert decode(dims(dt=3)) == ERR["PKV_ERR_DTYPE"]
+    assert rac(dims(dt=3)) == ERR["PKV_ERR_DTYPE"]
     assert cb(dims(Hkv=0)) == ERR["PKV_ERR_HEADS"]
     assert cb(d, n=-1) == ERR["PKV_ERR_SHAPE"]
     assert cb(d, mp=None) == ERR["PKV_ERR_NULL"]

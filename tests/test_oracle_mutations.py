@@ -10,6 +10,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_oracle.c")
@@ -41,6 +42,13 @@ MUTANTS = {
                         "uint32_t u = (uint32_t)b << 15;"),
     "query_head_ignored": ("qbase = ((size_t)s * jb->num_heads + h) * hd;",
                            "qbase = ((size_t)s * jb->num_heads) * hd;"),
+    "e4m3_exponent_bias": ("ldexp((double)(8 + fr), ex - 10)",
+                           "ldexp((double)(8 + fr), ex - 11)"),
+    "e4m3_ties_to_odd": ("(a - vlo == vhi - a && (lo & 1))",
+                         "(a - vlo == vhi - a && !(lo & 1))"),
+    "key_scale_dropped": ("              jb->k_scale);", "              1.0);"),
+    "cache_scale_multiplied": ("e4m3_encode(xk / jb->k_scale)",
+                               "e4m3_encode(xk * jb->k_scale)"),
 }
 
 
@@ -57,6 +65,13 @@ def _pin_calls():
     ]
     calls += [lambda a=a: pins.test_cache_write_matches_numpy_view_scatter(*a)
               for a in [("f32", 16, 64), ("bf16", 8, 8)]]
+    calls += [fp8pins.test_decode_every_code,
+              fp8pins.test_encode_matches_library_in_range_including_ties,
+              fp8pins.test_encode_saturates_and_keeps_nan]
+    calls += [lambda a=a: fp8pins.test_quantising_cache_write_matches_view_scatter(*a)
+              for a in [("bf16", 1.0), ("f16", 0.05)]]
+    calls += [lambda a=a: fp8pins.test_decode_on_quantised_cache_is_attention_on_dequantised_values(*a)
+              for a in [("bf16", 8, 2)]]
     return calls
 
 
@@ -64,7 +79,9 @@ def _pin_calls():
 def test_planted_mistake_is_caught(name, tmp_path):
     old, new = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    # a mistake in a formula the oracle writes out more than once is planted
+    # everywhere that formula appears
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
     mutated = tmp_path / "mut.c"
     mutated.write_text(src.replace(old, new))
     lib = tmp_path / "libmut.so"
