@@ -17,6 +17,10 @@ Prints one JSON line on stdout:
 
     python bench.py [--steps K] [--warmup W] [--workload mha13b]
                     [--variant single|split] [--partition 512]
+                    [--kv-dtype same|fp8]
+
+With --kv-dtype fp8 the caches hold 8-bit E4M3 values (per-tensor scales
+of 1); the queries and outputs keep the workload's dtype.
 """
 from __future__ import annotations
 
@@ -50,6 +54,9 @@ def parse():
                             "shared_prefix_bs16", "shared_prefix_bs32"])
     p.add_argument("--variant", default="single", choices=["single", "split"])
     p.add_argument("--partition", type=int, default=512)
+    p.add_argument("--kv-dtype", default="same", choices=["same", "fp8"],
+                   help="cache element type: the workload's (default) or "
+                        "8-bit E4M3")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--mode", default="decode", choices=["decode", "copy_blocks"],
@@ -112,6 +119,8 @@ def main():
 
     tdt = {"f32": torch.float32, "f16": torch.float16,
            "bf16": torch.bfloat16}[w.dtype]
+    fp8 = args.kv_dtype == "fp8"
+    cdt = torch.float8_e4m3fn if fp8 else tdt
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -125,7 +134,7 @@ def main():
     new_k, new_v = dev(w.new_k()), dev(w.new_v())
     new_slots = torch.from_numpy(w.new_slots()).cuda()
     k_cache, v_cache = pkv.new_kv_cache(w.num_blocks, w.num_kv_heads,
-                                        w.block_size, w.head_dim, tdt, fill=0.0)
+                                        w.block_size, w.head_dim, cdt, fill=0.0)
     # prefill: every earlier token written by the library's cache write
     kk, vv = dev(w.kv_k), dev(w.kv_v)
     pkv.reshape_and_cache(kk, vv, k_cache, v_cache,
@@ -175,18 +184,10 @@ def main():
     att_ms = [e[1].elapsed_time(e[2]) for e in ev]
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms")
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {n} bytes done")
+    calibration_copy(args.calib_copy_mib)
 
     e = np.dtype(wl.STORAGE[w.dtype]).itemsize
-    kv_bytes = w.kv_bytes()
+    kv_bytes = w.kv_bytes(1 if fp8 else None)
     nblk = int(sum(-(-int(L) // w.block_size) for L in w.context_lens))
     qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
     table_bytes = 4 * nblk + 4 * w.num_seqs
@@ -197,10 +198,11 @@ def main():
     tok_s = w.num_seqs / (ms_step * 1e-3)
     kernel = ("decode_vector_kernel" if w.num_heads == w.num_kv_heads
               or w.dtype == "f32" else "decode_mfma_kernel")
+    tag = w.name + ("_fp8" if fp8 else "")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(kernel, w.name),
+                "traffic": stored_traffic(kernel, tag),
                 "kernel": kernel + ("" if args.variant == "single"
                                     else " + partition_reduce_kernel"),
                 "algorithmic_bytes_per_launch": att_alg_bytes,
@@ -208,13 +210,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, kv_bytes)
+        cpu = cpu_baseline(w, kv_bytes, fp8)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{w.dtype}, e4m3 kv" if fp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs,
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
@@ -222,6 +225,7 @@ def main():
                    "num_blocks": w.num_blocks, "seed": args.seed,
                    "mean_context": float(w.context_lens.mean()),
                    "variant": args.variant,
+                   "kv_dtype": "e4m3" if fp8 else w.dtype,
                    "partition": args.partition if args.variant == "split" else None,
                    "accumulate": "f32", "kv_bytes_per_step": kv_bytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -234,6 +238,22 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def calibration_copy(mib: int):
+    """One plain device copy of `mib` MiB, so that HBM counters read in the
+    same run can be scaled to bytes."""
+    if not mib:
+        return
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {n} bytes done")
 
 
 def bench_copy_blocks(args):
@@ -264,6 +284,7 @@ def bench_copy_blocks(args):
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
+    calibration_copy(args.calib_copy_mib)
     block_bytes = hkv * bs * d * 2
     moved = 2 * 2 * n * block_bytes            # K and V, read and written
     gbs = moved / (ms * 1e-3) / 1e9
@@ -298,7 +319,7 @@ def bench_copy_blocks(args):
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, kv_bytes):
+def cpu_baseline(w, kv_bytes, fp8=False):
     """The oracle, as it stands, on host cores: the same decode step (the
     cache write of the new tokens, then attention for every sequence and
     head).  The pool it reads is built untimed beforehand."""
@@ -308,20 +329,29 @@ def cpu_baseline(w, kv_bytes):
 
     threads = oracle.default_threads()
     t0 = time.time()
+    cdt = "fp8" if fp8 else w.dtype
     kc, vc = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
-                             w.head_dim, w.dtype, fill="zero")
-    oracle.reshape_and_cache(w.kv_k, w.kv_v, kc, vc, w.prefill_slots(),
-                             w.num_kv_heads, w.head_dim, w.block_size,
-                             w.num_blocks, w.dtype)
+                             w.head_dim, cdt, fill="zero")
+
+    def write(k, v, slots):
+        if fp8:
+            oracle.reshape_and_cache_fp8(k, v, kc, vc, slots, w.num_kv_heads,
+                                         w.head_dim, w.block_size,
+                                         w.num_blocks, w.dtype, 1.0, 1.0)
+        else:
+            oracle.reshape_and_cache(k, v, kc, vc, slots, w.num_kv_heads,
+                                     w.head_dim, w.block_size, w.num_blocks,
+                                     w.dtype)
+
+    write(w.kv_k, w.kv_v, w.prefill_slots())
     log(f"[bench] oracle pool built in {time.time()-t0:.1f}s; timing the "
         f"oracle on {threads} threads")
     t1 = time.perf_counter()
-    oracle.reshape_and_cache(w.new_k(), w.new_v(), kc, vc, w.new_slots(),
-                             w.num_kv_heads, w.head_dim, w.block_size,
-                             w.num_blocks, w.dtype)
+    write(w.new_k(), w.new_v(), w.new_slots())
     out = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.context_lens,
                               w.scale, w.block_size, w.num_kv_heads,
-                              w.num_blocks, w.dtype, threads=threads)
+                              w.num_blocks, w.dtype, threads=threads,
+                              cache_dtype="fp8" if fp8 else None)
     dt = time.perf_counter() - t1
     assert np.all(np.isfinite(out))
     log(f"[bench] oracle step {dt:.2f}s")

@@ -142,9 +142,11 @@ class Workload:
         out[ok] = self.kv_slots[self.new_rows[ok]]
         return out
 
-    def kv_bytes(self) -> int:
-        """K and V bytes of every live token, each KV head once."""
-        e = np.dtype(STORAGE[self.dtype]).itemsize
+    def kv_bytes(self, elem_bytes: int | None = None) -> int:
+        """K and V bytes of every live token, each KV head once; elements of
+        the workload's dtype unless `elem_bytes` says otherwise (1 for an
+        8-bit cache)."""
+        e = elem_bytes or np.dtype(STORAGE[self.dtype]).itemsize
         return int(self.context_lens.astype(np.int64).sum()) * \
             self.num_kv_heads * self.head_dim * e * 2
 
