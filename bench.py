@@ -59,9 +59,11 @@ def parse():
                         "8-bit E4M3")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--mode", default="decode", choices=["decode", "copy_blocks"],
+    p.add_argument("--mode", default="decode",
+                   choices=["decode", "copy_blocks", "swap"],
                    help="decode: the decode step (default); copy_blocks: the "
-                        "copy-on-write block copy")
+                        "copy-on-write block copy; swap: blocks out to pinned "
+                        "host memory and back")
     p.add_argument("--pairs", type=int, default=2048,
                    help="copy_blocks mode: block pairs copied per launch")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -111,6 +113,8 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy_blocks":
         return bench_copy_blocks(args)
+    if args.mode == "swap":
+        return bench_swap(args)
     t0 = time.time()
     w = wl.CONFIGS[args.workload](args.seed)
     log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_heads} "
@@ -316,6 +320,94 @@ def bench_copy_blocks(args):
                         "algorithmic_bytes_per_launch": moved,
                         "mean_launch_ms": round(ms, 5)},
            "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args):
+    """Swapping: `pairs` scattered blocks of the 13B-class shape (40 KV
+    heads, 16-token blocks, head_dim 128, fp16: 160 KiB per block per pool)
+    copied from the device pools to pinned host pools (out), then back into
+    other device blocks (in), one swap_blocks launch each.  For context, the
+    same blocks moved by one DMA copy per block (torch copy_, non-blocking)
+    and one contiguous DMA copy of the same byte count."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_309_amd as pkv
+
+    nb, hkv, bs, d = 2048, 40, 16, 128
+    n = min(args.pairs, nb // 2)
+    kd, vd = pkv.new_kv_cache(nb, hkv, bs, d, torch.float16, fill=1.0)
+    hk, hv = pkv.new_kv_cache(n, hkv, bs, d, torch.float16, device="cpu",
+                              pin_memory=True, fill=0.0)
+    rng = np.random.default_rng(args.seed)
+    perm = rng.permutation(nb)
+    out_pairs = np.stack([perm[:n], np.arange(n)], 1).astype(np.int64)
+    in_pairs = np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)
+    m_out = torch.from_numpy(out_pairs).cuda()
+    m_in = torch.from_numpy(in_pairs).cuda()
+    stream = torch.cuda.current_stream()
+    block_bytes = hkv * bs * d * 2
+    moved = 2 * n * block_bytes                # K and V, one direction
+
+    def timed(fn, steps):
+        for _ in range(max(1, args.warmup // 4)):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    steps = max(1, min(args.steps, 20))
+    ms_out = timed(lambda: pkv.swap_blocks(kd, vd, hk, hv, m_out), steps)
+    ms_in = timed(lambda: pkv.swap_blocks(hk, hv, kd, vd, m_in), steps)
+
+    def per_block_dma():
+        for s_, t_ in out_pairs[:, :].tolist():
+            hk[t_].copy_(kd[s_], non_blocking=True)
+            hv[t_].copy_(vd[s_], non_blocking=True)
+    ms_dma = timed(per_block_dma, max(1, steps // 4))
+    flat = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    src = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    ms_flat = timed(lambda: flat.copy_(src, non_blocking=True), steps)
+    calibration_copy(args.calib_copy_mib)
+
+    # the copies are bit copies: one sampled block checked after the run
+    torch.cuda.synchronize()
+    assert torch.equal(hk[0].cuda(), kd[int(out_pairs[0, 0])])
+
+    gbs = lambda ms: moved / (ms * 1e-3) / 1e9
+    both = 2 * moved / ((ms_out + ms_in) * 1e-3) / 1e9
+    rec = {"metric": "swap_blocks GB/s over the host link (K and V blocks, "
+                     "device to pinned host and back)",
+           "value": round(both, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_out + ms_in, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": "swap", "pairs": n, "num_blocks": nb,
+                      "num_kv_heads": hkv, "block_size": bs, "head_dim": d,
+                      "block_bytes_per_pool": block_bytes,
+                      "bytes_each_way": moved},
+           "swap_out_gbs": round(gbs(ms_out), 2),
+           "swap_in_gbs": round(gbs(ms_in), 2),
+           "context": {"dma_one_copy_per_block_out_gbs": round(gbs(ms_dma), 2),
+                       "dma_contiguous_out_gbs": round(gbs(ms_flat), 2)},
+           "roofline": {"bound": "host_link", "achieved": round(both, 2),
+                        "peak": HOST_LINK_GBS, "unit": "GB/s",
+                        "frac": round(both / HOST_LINK_GBS, 4),
+                        "traffic": None, "kernel": "copy_blocks_kernel",
+                        "algorithmic_bytes_per_launch": moved,
+                        "mean_launch_ms": round((ms_out + ms_in) / 2, 4)},
+           "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
 

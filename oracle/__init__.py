@@ -96,6 +96,10 @@ def _load(path: str | None = None):
                                                ctypes.c_int]
             lib.oracle_widen.restype = ctypes.c_int
             lib.oracle_widen.argtypes = [P, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_swap_blocks.restype = ctypes.c_int
+            lib.oracle_swap_blocks.argtypes = [
+                P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_int64, ctypes.c_int]
             if path is not None:
                 return lib
             _lib = lib
@@ -256,6 +260,22 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, mapping,
     _check(_load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(mp),
                                       mp.shape[0], num_blocks, block_elems,
                                       DTYPES[dtype]))
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray,
+                dst_v: np.ndarray, mapping, src_num_blocks: int,
+                dst_num_blocks: int, dtype: str) -> None:
+    """Swapping: block mapping[i][1] of the destination flat pools becomes a
+    copy of block mapping[i][0] of the source pools, in place."""
+    mp = np.ascontiguousarray(mapping, dtype=np.int64).reshape(-1, 2)
+    assert src_k.size == src_v.size and dst_k.size == dst_v.size
+    block_elems = src_k.size // max(src_num_blocks, 1)
+    assert block_elems * src_num_blocks == src_k.size
+    assert block_elems * dst_num_blocks == dst_k.size
+    _check(_load().oracle_swap_blocks(
+        _ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(mp),
+        mp.shape[0], src_num_blocks, dst_num_blocks, max(block_elems, 1),
+        DTYPES[dtype]))
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -526,6 +526,45 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *mapping,
   return OR_OK;
 }
 
+/* Swapping: under memory pressure a request's blocks can be moved out of
+ * device memory and later back, as an operating system evicts pages ("PagedAttention
+ * - Virtual Memory for the KV Cache" explainer, chapter 05, card "Preemption &
+ * swapping"; deep dive, card "What Indirection Buys").  For each pair i,
+ * block mapping[2i+1] of the destination pools becomes a byte copy of block
+ * mapping[2i] of the source pools (distinct pools).  Rejected (no write):
+ * an index outside its pool, or a destination that appears twice. */
+int oracle_swap_blocks(const void *src_k, const void *src_v, void *dst_k,
+                       void *dst_v, const int64_t *mapping, int64_t num_pairs,
+                       int64_t src_num_blocks, int64_t dst_num_blocks,
+                       int64_t block_elems, int dtype) {
+  if (num_pairs < 0 || src_num_blocks < 0 || dst_num_blocks < 0 ||
+      block_elems <= 0 || dtype < OR_F32 || dtype > OR_FP8)
+    return OR_ERR_ARG;
+  unsigned char *dst_seen = calloc((size_t)dst_num_blocks + 1, 1);
+  if (!dst_seen)
+    return OR_ERR_NOMEM;
+  int rc = OR_OK;
+  for (int64_t i = 0; i < num_pairs && rc == OR_OK; ++i) {
+    int64_t s = mapping[2 * i], d = mapping[2 * i + 1];
+    if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
+      rc = OR_ERR_TABLE;
+    else if (dst_seen[d])
+      rc = OR_ERR_SLOT_DUP;
+    else
+      dst_seen[d] = 1;
+  }
+  free(dst_seen);
+  if (rc != OR_OK)
+    return rc;
+  const size_t bytes = (size_t)block_elems * (size_t)elem_bytes(dtype);
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    size_t s = (size_t)mapping[2 * i], d = (size_t)mapping[2 * i + 1];
+    memcpy((char *)dst_k + d * bytes, (const char *)src_k + s * bytes, bytes);
+    memcpy((char *)dst_v + d * bytes, (const char *)src_v + s * bytes, bytes);
+  }
+  return OR_OK;
+}
+
 /* ---- 8-bit cache ----------------------------------------------------------
  * Lower-precision cache formats reduce the bytes per element ("PagedAttention:
  * how vLLM manages the KV cache", section "Keep the tensor formula beside the

@@ -10,6 +10,8 @@ Cache tensors (allocate them with new_kv_cache):
     v_cache  [num_blocks, num_kv_heads, block_size // 4, head_dim, 4]
 Caches of dtype torch.float8_e4m3fn hold 8-bit E4M3 codes with one scale per
 pool (k_scale, v_scale); the calls then route to the *_fp8 entry points.
+Host pools for swapped-out blocks (new_kv_cache(..., device="cpu",
+pin_memory=True)) have the same layouts in pinned host memory.
 """
 from __future__ import annotations
 
@@ -22,8 +24,8 @@ from ._lib import PkvDims, PkvError
 
 __all__ = ["reshape_and_cache", "paged_attention_decode",
            "paged_attention_decode_split", "split_workspace_bytes",
-           "new_kv_cache", "copy_blocks", "BlockManager", "PkvError",
-           "version"]
+           "new_kv_cache", "copy_blocks", "swap_blocks", "BlockManager",
+           "PkvError", "version"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
            torch.bfloat16: _lib.PKV_BF16}
@@ -54,12 +56,13 @@ def _dtype(t: torch.Tensor) -> int:
 
 def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int,
                  head_dim: int, dtype: torch.dtype, device="cuda",
-                 fill: float | None = None):
-    """Allocate (k_cache, v_cache) in the library's block layouts."""
+                 fill: float | None = None, pin_memory: bool = False):
+    """Allocate (k_cache, v_cache) in the library's block layouts (on the
+    host with pin_memory=True: a pool that swap_blocks can reach)."""
     k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim),
-                    dtype=dtype, device=device)
+                    dtype=dtype, device=device, pin_memory=pin_memory)
     v = torch.empty((num_blocks, num_kv_heads, block_size // 4, head_dim, 4),
-                    dtype=dtype, device=device)
+                    dtype=dtype, device=device, pin_memory=pin_memory)
     if fill is not None:
         k.fill_(fill)
         v.fill_(fill)
@@ -176,17 +179,39 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
         bs, ctypes.byref(dims), _stream(stream)))
 
 
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor,
+                dst_k: torch.Tensor, dst_v: torch.Tensor,
+                block_mapping: torch.Tensor, stream=None) -> None:
+    """Block block_mapping[i, 1] of (dst_k, dst_v) becomes a copy of block
+    block_mapping[i, 0] of (src_k, src_v); each pool is on the GPU or in
+    pinned host memory, and the mapping (int64 [n, 2]) on the GPU or pinned.
+    Asynchronous: synchronise the stream before reading a host pool."""
+    if src_k.dtype != dst_k.dtype or src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("source and destination pools differ in shape")
+    NB, Hkv, bs, D = src_k.shape
+    dt = _lib.PKV_E4M3 if _is_fp8(src_k) else _dtype(src_k)
+    dims = PkvDims(0, Hkv, Hkv, D, 0, 0, dt)
+    n = block_mapping.shape[0] if block_mapping.numel() else 0
+    _lib.check(_lib.lib().swap_blocks(
+        _ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v),
+        _ptr(block_mapping) if n else None, n, NB, dst_k.shape[0], bs,
+        ctypes.byref(dims), _stream(stream)))
+
+
 class BlockManager:
     """Host block manager of the paged cache (free list, reference counts,
-    block tables, copy-on-write), a thin wrapper of the pkv_bm_* calls."""
+    block tables, copy-on-write, swapping to a host pool), a thin wrapper of
+    the pkv_bm_* calls."""
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int,
+                 num_host_blocks: int = 0):
         import numpy as np
         self._np = np
         self._h = ctypes.c_void_p()
-        _lib.check(_lib.lib().pkv_bm_create(num_blocks, block_size,
-                                            ctypes.byref(self._h)))
+        _lib.check(_lib.lib().pkv_bm_create_with_host(
+            num_blocks, num_host_blocks, block_size, ctypes.byref(self._h)))
         self.num_blocks = num_blocks
+        self.num_host_blocks = num_host_blocks
         self.block_size = block_size
 
     def close(self) -> None:
@@ -246,6 +271,44 @@ class BlockManager:
 
     def num_tokens(self, seq_id: int) -> int:
         return _lib.lib().pkv_bm_num_tokens(self._h, seq_id)
+
+    def _move(self, fn, seq_ids):
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        cap = max(self.num_blocks, self.num_host_blocks, 1)
+        pairs = np.empty((cap, 2), np.int64)
+        k = ctypes.c_int32(0)
+        _lib.check(fn(self._h, ids.ctypes.data, ids.shape[0],
+                      pairs.ctypes.data, cap, ctypes.byref(k)))
+        return pairs[:k.value]
+
+    def swap_out(self, seq_ids):
+        """Move the sequences to the host pool: returns the (device block,
+        host block) pairs [k, 2] to copy with swap_blocks."""
+        return self._move(_lib.lib().pkv_bm_swap_out, seq_ids)
+
+    def swap_in(self, seq_ids):
+        """Bring swapped-out sequences back: (host block, device block)
+        pairs [k, 2] to copy with swap_blocks."""
+        return self._move(_lib.lib().pkv_bm_swap_in, seq_ids)
+
+    def num_free_host_blocks(self) -> int:
+        return _lib.lib().pkv_bm_num_free_host_blocks(self._h)
+
+    def host_refcount(self, block: int) -> int:
+        return _lib.lib().pkv_bm_host_refcount(self._h, block)
+
+    def is_swapped(self, seq_id: int) -> int:
+        return _lib.lib().pkv_bm_is_swapped(self._h, seq_id)
+
+    def block_table(self, seq_id: int):
+        np = self._np
+        cap = max(self.num_blocks, self.num_host_blocks, 1)
+        t = np.empty(cap, np.int32)
+        k = ctypes.c_int32(0)
+        _lib.check(_lib.lib().pkv_bm_block_table(
+            self._h, seq_id, t.ctypes.data, cap, ctypes.byref(k)))
+        return t[:k.value]
 
 
 # load (and fail loudly) at import

@@ -19,6 +19,7 @@ STATUS = {
     9: "PKV_ERR_WORKSPACE", 10: "PKV_ERR_LAUNCH", 11: "PKV_ERR_ALIAS",
     12: "PKV_ERR_NO_BLOCKS", 13: "PKV_ERR_UNKNOWN_SEQ",
     14: "PKV_ERR_SEQ_EXISTS", 15: "PKV_ERR_CAPACITY", 16: "PKV_ERR_SCALE",
+    17: "PKV_ERR_SWAPPED", 18: "PKV_ERR_SHARED", 19: "PKV_ERR_MEMORY",
 }
 
 # every function include/*.h declares
@@ -30,7 +31,10 @@ EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "copy_blocks", "pkv_bm_create", "pkv_bm_destroy",
            "pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_tokens",
            "pkv_bm_free_sequence", "pkv_bm_batch_tables",
-           "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_bm_num_tokens")
+           "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_bm_num_tokens",
+           "swap_blocks", "pkv_bm_create_with_host", "pkv_bm_swap_out",
+           "pkv_bm_swap_in", "pkv_bm_num_free_host_blocks",
+           "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table")
 
 
 class PkvDims(ctypes.Structure):
@@ -98,6 +102,22 @@ def load() -> ctypes.CDLL:
     lib.pkv_bm_refcount.argtypes = [P, I32]
     lib.pkv_bm_num_tokens.restype = I32
     lib.pkv_bm_num_tokens.argtypes = [P, I64]
+    lib.swap_blocks.restype = I
+    lib.swap_blocks.argtypes = [P, P, P, P, P, I, I32, I32, I, D, P]
+    lib.pkv_bm_create_with_host.restype = I
+    lib.pkv_bm_create_with_host.argtypes = [I32, I32, I32, ctypes.POINTER(P)]
+    lib.pkv_bm_swap_out.restype = I
+    lib.pkv_bm_swap_out.argtypes = [P, P, I32, P, I32, ctypes.POINTER(I32)]
+    lib.pkv_bm_swap_in.restype = I
+    lib.pkv_bm_swap_in.argtypes = [P, P, I32, P, I32, ctypes.POINTER(I32)]
+    lib.pkv_bm_num_free_host_blocks.restype = I32
+    lib.pkv_bm_num_free_host_blocks.argtypes = [P]
+    lib.pkv_bm_host_refcount.restype = I32
+    lib.pkv_bm_host_refcount.argtypes = [P, I32]
+    lib.pkv_bm_is_swapped.restype = I32
+    lib.pkv_bm_is_swapped.argtypes = [P, I64]
+    lib.pkv_bm_block_table.restype = I
+    lib.pkv_bm_block_table.argtypes = [P, I64, P, I32, ctypes.POINTER(I32)]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_version.restype = I

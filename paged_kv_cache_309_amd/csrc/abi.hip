@@ -1,6 +1,7 @@
 // abi.hip - the exported C ABI: argument validation, kernel choice and
-// launch.  Every check runs before the first HIP call, so a rejected call
-// touches no device.
+// launch.  Every check on plain arguments runs before the first HIP call, so
+// a call rejected by one touches no device; swap_blocks then asks the
+// runtime what its pointers are.
 #include <limits.h>
 #include <stdint.h>
 
@@ -22,6 +23,34 @@ int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_E4M3 ? 1
 constexpr int kCacheSame = -1;  // the caches hold dims->dtype
 
 bool scale_ok(float x) { return x > 0.f && x <= 3.0e38f; }  // finite, positive
+
+// The address a kernel uses for p: p itself for device (or managed)
+// memory; for pinned host memory, the device-side address of the same byte.
+// False for anything else (pageable host memory, unknown pointers).
+bool device_address(const void *p, void **out) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error this query leaves behind
+    return false;
+  }
+  switch (at.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+      *out = const_cast<void *>(p);
+      return true;
+    case hipMemoryTypeHost: {
+      void *d = nullptr;
+      if (hipHostGetDevicePointer(&d, const_cast<void *>(p), 0) != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return false;
+      }
+      *out = d;
+      return true;
+    }
+    default:
+      return false;
+  }
+}
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   if (na == 0 || nb == 0) return false;
@@ -336,11 +365,60 @@ int copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
       overlap(block_mapping, (size_t)num_pairs * 16, v_cache, (size_t)cb))
     return PKV_ERR_ALIAS;
   pkv::CopyBlocksArgs a{};
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.src_k = k_cache;
+  a.src_v = v_cache;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
   a.block_mapping = block_mapping;
   a.block_bytes = (int64_t)bb;
-  a.num_blocks = dims->num_blocks;
+  a.src_num_blocks = dims->num_blocks;
+  a.dst_num_blocks = dims->num_blocks;
+  const hipError_t err =
+      pkv::launch_copy_blocks(a, num_pairs, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int swap_blocks(const void *src_k_cache, const void *src_v_cache, void *dst_k_cache,
+                void *dst_v_cache, const int64_t *block_mapping, int num_pairs,
+                int32_t src_num_blocks, int32_t dst_num_blocks, int block_size,
+                const pkv_dims *dims, pkv_stream_t stream) {
+  if (!dims) return PKV_ERR_NULL;
+  if (dims->dtype < PKV_F32 || dims->dtype > PKV_E4M3) return PKV_ERR_DTYPE;
+  if (block_size != 16 && block_size != 32) return PKV_ERR_BLOCK_SIZE;
+  if (dims->head_dim != 64 && dims->head_dim != 128) return PKV_ERR_HEAD_DIM;
+  if (dims->num_kv_heads <= 0) return PKV_ERR_HEADS;
+  if (num_pairs < 0 || src_num_blocks < 0 || dst_num_blocks < 0) return PKV_ERR_SHAPE;
+  const u128 bb = (u128)dims->num_kv_heads * (u128)block_size * (u128)dims->head_dim *
+                  (u128)elem_bytes(dims->dtype);
+  const u128 sb = bb * (u128)src_num_blocks, db = bb * (u128)dst_num_blocks;
+  if (sb > ((u128)1 << 62) || db > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_k_cache || !src_v_cache || !dst_k_cache || !dst_v_cache || !block_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned16(src_k_cache) || !aligned16(src_v_cache) || !aligned16(dst_k_cache) ||
+      !aligned16(dst_v_cache) || !aligned(block_mapping, 8))
+    return PKV_ERR_ALIGN;
+  const size_t mb = (size_t)num_pairs * 16;
+  if (overlap(dst_k_cache, (size_t)db, dst_v_cache, (size_t)db) ||
+      overlap(block_mapping, mb, dst_k_cache, (size_t)db) ||
+      overlap(block_mapping, mb, dst_v_cache, (size_t)db))
+    return PKV_ERR_ALIAS;
+  // Every pointer must be one the device can address: device memory, or
+  // pinned host memory (then its device-side address is used).
+  const void *ptrs[5] = {src_k_cache, src_v_cache, dst_k_cache, dst_v_cache, block_mapping};
+  void *dev[5];
+  for (int i = 0; i < 5; ++i) {
+    if (!device_address(ptrs[i], &dev[i])) return PKV_ERR_MEMORY;
+  }
+  pkv::CopyBlocksArgs a{};
+  a.src_k = dev[0];
+  a.src_v = dev[1];
+  a.dst_k = dev[2];
+  a.dst_v = dev[3];
+  a.block_mapping = static_cast<const int64_t *>(dev[4]);
+  a.block_bytes = (int64_t)bb;
+  a.src_num_blocks = src_num_blocks;
+  a.dst_num_blocks = dst_num_blocks;
   const hipError_t err =
       pkv::launch_copy_blocks(a, num_pairs, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
@@ -365,10 +443,13 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_SEQ_EXISTS: return "sequence id already in use";
     case PKV_ERR_CAPACITY: return "output buffer too small";
     case PKV_ERR_SCALE: return "a dequantisation scale is not a finite positive number";
+    case PKV_ERR_SWAPPED: return "sequence is swapped out (or, for swap_in, is not)";
+    case PKV_ERR_SHARED: return "a block is shared with a sequence outside the list";
+    case PKV_ERR_MEMORY: return "a pointer is neither device memory nor pinned host memory";
     default: return "unknown status";
   }
 }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 200; }
 
 }  // extern "C"

@@ -14,14 +14,15 @@ constexpr int64_t kCopyChunk = kCopyThreads * kCopyUnroll * 16;    // bytes per 
 
 // grid: x = pair, y = pool (0: K, 1: V), z = chunk of the block.  Every
 // block is one contiguous run of block_bytes in each pool, whatever the
-// layout inside it, so the copy is a plain 16-byte streaming copy.
+// layout inside it, so the copy is a plain 16-byte streaming copy.  Either
+// side may be pinned host memory mapped into the device's address space
+// (swapping): the same loads and stores then cross the host link.
 __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(CopyBlocksArgs a) {
   const int64_t src = a.block_mapping[2 * (int64_t)blockIdx.x];
   const int64_t dst = a.block_mapping[2 * (int64_t)blockIdx.x + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  char *base = static_cast<char *>(blockIdx.y ? a.v_cache : a.k_cache);
-  const char *s = base + src * a.block_bytes;
-  char *d = base + dst * a.block_bytes;
+  if (src < 0 || src >= a.src_num_blocks || dst < 0 || dst >= a.dst_num_blocks) return;
+  const char *s = static_cast<const char *>(blockIdx.y ? a.src_v : a.src_k) + src * a.block_bytes;
+  char *d = static_cast<char *>(blockIdx.y ? a.dst_v : a.dst_k) + dst * a.block_bytes;
   for (int64_t off = (int64_t)blockIdx.z * kCopyChunk; off < a.block_bytes;
        off += (int64_t)gridDim.z * kCopyChunk) {
     u32x4 x[kCopyUnroll];

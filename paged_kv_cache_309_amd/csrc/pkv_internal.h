@@ -49,12 +49,17 @@ struct CacheWriteArgs {
   float v_scale;
 };
 
+// Block copies between pools (the same pools for copy-on-write; a device
+// and a pinned host pool for swapping).  Pointers are device addresses.
 struct CopyBlocksArgs {
-  void *k_cache;
-  void *v_cache;
+  const void *src_k;
+  const void *src_v;
+  void *dst_k;
+  void *dst_v;
   const int64_t *block_mapping;  // [num_pairs, 2] (source, destination)
   int64_t block_bytes;           // bytes of one block in one pool
-  int num_blocks;
+  int src_num_blocks;
+  int dst_num_blocks;
 };
 
 // Each returns the launch error (hipSuccess when enqueued).

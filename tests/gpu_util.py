@@ -146,10 +146,14 @@ def oracle_out(w: wl.Workload, kc, vc, sel=None, q=None):
 def pool_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bits of a device pool, flat."""
     t = t.detach().contiguous().view(-1)
+    if t.element_size() == 1:
+        return t.view(torch.uint8).cpu().numpy()
     if t.element_size() == 2:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
 
 
 def host_bits(a: np.ndarray) -> np.ndarray:
+    if a.dtype.itemsize == 1:
+        return a.view(np.uint8)
     return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == 200
     for code in S:
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(999) == b"unknown status"
@@ -150,3 +150,28 @@ def test_copy_blocks_rejects_bad_arguments():
     assert cb(d, mp=C + 4) == ERR["PKV_ERR_ALIGN"]
     assert cb(d, vc=A) == ERR["PKV_ERR_ALIAS"]
     assert cb(d, n=0, kc=None, vc=None, mp=None) == 0
+
+
+def test_swap_blocks_rejects_bad_arguments():
+    """Checks that return before the runtime is asked about the pointers."""
+    lib = _lib.lib()
+
+    def sw(d, n=4, bs=16, sk=A, sv=B, dk=C, dv=DQ, mp=E, snb=64, dnb=32):
+        return lib.swap_blocks(sk, sv, dk, dv, mp, n, snb, dnb, bs,
+                               ctypes.byref(d), None)
+    d = dims()
+    assert sw(d, bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
+    assert sw(dims(D=32)) == ERR["PKV_ERR_HEAD_DIM"]
+    assert sw(dims(dt=5)) == ERR["PKV_ERR_DTYPE"]
+    assert sw(dims(Hkv=0)) == ERR["PKV_ERR_HEADS"]
+    assert sw(d, n=-1) == ERR["PKV_ERR_SHAPE"]
+    assert sw(d, snb=-1) == ERR["PKV_ERR_SHAPE"]
+    assert sw(d, dnb=-2) == ERR["PKV_ERR_SHAPE"]
+    assert sw(d, mp=None) == ERR["PKV_ERR_NULL"]
+    assert sw(d, dv=None) == ERR["PKV_ERR_NULL"]
+    assert sw(d, sk=A + 8) == ERR["PKV_ERR_ALIGN"]
+    assert sw(d, mp=E + 4) == ERR["PKV_ERR_ALIGN"]
+    # destination pools of 32 blocks x 2 x 16 x 128 x 2 B = 256 KiB each
+    assert sw(d, dv=C + 4096) == ERR["PKV_ERR_ALIAS"]
+    assert sw(d, mp=C + 64) == ERR["PKV_ERR_ALIAS"]
+    assert sw(d, n=0, sk=None, sv=None, dk=None, dv=None, mp=None) == 0

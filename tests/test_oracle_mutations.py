@@ -10,6 +10,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_blocks as blockpins
 import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
 
@@ -49,6 +50,12 @@ MUTANTS = {
     "key_scale_dropped": ("              jb->k_scale);", "              1.0);"),
     "cache_scale_multiplied": ("e4m3_encode(xk / jb->k_scale)",
                                "e4m3_encode(xk * jb->k_scale)"),
+    "copy_blocks_reversed": (
+        "memcpy((char *)k_cache + d * bytes, (const char *)k_cache + s * bytes, bytes);",
+        "memcpy((char *)k_cache + s * bytes, (const char *)k_cache + d * bytes, bytes);"),
+    "swap_values_from_keys": (
+        "memcpy((char *)dst_v + d * bytes, (const char *)src_v + s * bytes, bytes);",
+        "memcpy((char *)dst_v + d * bytes, (const char *)src_k + s * bytes, bytes);"),
 }
 
 
@@ -72,6 +79,9 @@ def _pin_calls():
               for a in [("bf16", 1.0), ("f16", 0.05)]]
     calls += [lambda a=a: fp8pins.test_decode_on_quantised_cache_is_attention_on_dequantised_values(*a)
               for a in [("bf16", 8, 2)]]
+    calls += [lambda: blockpins.test_copy_blocks_is_row_assignment("f32", 12, 2, 16, 64, 5),
+              lambda: blockpins.test_swap_blocks_is_row_assignment("bf16", 30, 10, 7),
+              blockpins.test_swap_blocks_round_trip_and_rejections]
     return calls
 
 
