@@ -96,6 +96,13 @@ def _load(path: str | None = None):
                                                ctypes.c_int]
             lib.oracle_widen.restype = ctypes.c_int
             lib.oracle_widen.argtypes = [P, P, ctypes.c_int64, ctypes.c_int]
+            lib.oracle_paged_prefill.restype = ctypes.c_int
+            lib.oracle_paged_prefill.argtypes = [
+                P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_float, ctypes.c_float, P,
+                ctypes.c_int64, ctypes.c_int]
             lib.oracle_swap_blocks.restype = ctypes.c_int
             lib.oracle_swap_blocks.argtypes = [
                 P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -218,6 +225,45 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         float(scale), block_size, S, Hq, num_kv_heads, D, num_blocks,
         bt.shape[1], DTYPES[dtype], DTYPES[cache_dtype], float(k_scale),
         float(v_scale), sel_ptr, nsel, threads or default_threads()))
+    return out
+
+
+def paged_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                  block_tables: np.ndarray, context_lens: np.ndarray,
+                  query_start_loc: np.ndarray, scale: float, block_size: int,
+                  num_kv_heads: int, num_blocks: int, dtype: str, sel=None,
+                  threads: int | None = None, cache_dtype: str | None = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Multi-query (chunked prefill) attention in float64.
+
+    q: [T, Hq, D] storage array of `dtype`, the query rows of sequence s
+    being query_start_loc[s] .. query_start_loc[s+1]-1, the last tokens of
+    its context (causal).  Returns [T, Hq, D] float64, or [N, D] for ``sel``
+    an [N, 2] array of (query row, head) pairs.
+    """
+    cache_dtype = cache_dtype or dtype
+    q = np.ascontiguousarray(q, dtype=STORAGE[dtype])
+    T, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    S = cl.shape[0]
+    assert bt.ndim == 2 and bt.shape[0] == S and qsl.shape == (S + 1,)
+    if sel is None:
+        out = np.empty((T, Hq, D), np.float64)
+        nsel, sel_ptr = 0, None
+    else:
+        sel_arr = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+        nsel = sel_arr.shape[0]
+        out = np.empty((nsel, D), np.float64)
+        sel_ptr = _ptr(sel_arr)
+    assert k_cache.dtype == STORAGE[cache_dtype]
+    _check(_load().oracle_paged_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+        _ptr(qsl), float(scale), block_size, S, T, Hq, num_kv_heads, D,
+        num_blocks, bt.shape[1], DTYPES[dtype], DTYPES[cache_dtype],
+        float(k_scale), float(v_scale), sel_ptr, nsel,
+        threads or default_threads()))
     return out
 
 

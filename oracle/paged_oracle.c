@@ -252,19 +252,23 @@ struct decode_job {
   int max_blocks_per_seq, dtype; /* dtype: of the caches */
   int q_dtype;                     /* of q */
   double k_scale, v_scale;         /* dequantisation scales of the caches */
-  const int32_t *sel; /* optional (seq, head) pairs */
+  const int32_t *sel; /* optional (seq, head) or (query row, head) pairs */
+  /* multi-query (chunked prefill): query rows of sequence s are
+   * query_start_loc[s] .. query_start_loc[s+1]-1; NULL for decode */
+  const int32_t *query_start_loc;
   int64_t num_items;
   int num_threads;
   int status; /* first error seen (written under the lock) */
   pthread_mutex_t lock;
 };
 
-/* One (sequence, query head): fills out[0 .. head_dim-1]. */
-static int decode_one(const struct decode_job *jb, int s, int h, double *out) {
+/* One query row `qrow` of sequence s and query head h, attending to the
+ * first L tokens of the sequence: fills out[0 .. head_dim-1]. */
+static int attend_one(const struct decode_job *jb, int s, int64_t qrow, int h,
+                      int L, double *out) {
   const int hd = jb->head_dim, bs = jb->block_size;
   const int group = jb->num_heads / jb->num_kv_heads;
   const int g = h / group;
-  const int L = jb->context_lens[s];
   for (int d = 0; d < hd; ++d)
     out[d] = 0.0;
   if (L <= 0)
@@ -273,7 +277,7 @@ static int decode_one(const struct decode_job *jb, int s, int h, double *out) {
     return OR_ERR_CONTEXT;
 
   const size_t hkv = (size_t)jb->num_kv_heads;
-  const size_t qbase = ((size_t)s * jb->num_heads + h) * hd;
+  const size_t qbase = ((size_t)qrow * jb->num_heads + h) * hd;
   const int32_t *table = jb->block_tables + (size_t)s * jb->max_blocks_per_seq;
 
   double *x = malloc(sizeof(double) * (size_t)L);
@@ -330,19 +334,36 @@ struct worker_arg {
   int tid;
 };
 
+/* Decode: the one query of sequence s sits at the end of its context and
+ * attends to all context_lens[s] tokens.  Multi-query: the C = (number of
+ * query rows of s) queries are the last C tokens of the context, in order,
+ * and query j attends to the tokens up to and including itself, i.e. the
+ * first context_lens[s] - C + j + 1 tokens (causal within the chunk). */
 static void *decode_worker(void *argp) {
   struct worker_arg *wa = argp;
   struct decode_job *jb = wa->jb;
   for (int64_t it = wa->tid; it < jb->num_items; it += jb->num_threads) {
-    int s, h;
+    int64_t r; /* query row: the sequence (decode) or a row of q */
+    int h;
     if (jb->sel) {
-      s = jb->sel[2 * it];
+      r = jb->sel[2 * it];
       h = jb->sel[2 * it + 1];
     } else {
-      s = (int)(it / jb->num_heads);
+      r = it / jb->num_heads;
       h = (int)(it % jb->num_heads);
     }
-    int rc = decode_one(jb, s, h, jb->out + (size_t)it * jb->head_dim);
+    int s = (int)r, L;
+    if (jb->query_start_loc) {
+      const int32_t *qsl = jb->query_start_loc;
+      s = 0;
+      while (s + 1 < jb->num_seqs && qsl[s + 1] <= r)
+        ++s;
+      const int64_t C = qsl[s + 1] - qsl[s];
+      L = (int)(jb->context_lens[s] - C + (r - qsl[s]) + 1);
+    } else {
+      L = jb->context_lens[s];
+    }
+    int rc = attend_one(jb, s, r, h, L, jb->out + (size_t)it * jb->head_dim);
     if (rc != OR_OK) {
       pthread_mutex_lock(&jb->lock);
       if (jb->status == OR_OK)
@@ -352,6 +373,47 @@ static void *decode_worker(void *argp) {
     }
   }
   return NULL;
+}
+
+/* Runs the job's items on jb->num_threads POSIX threads; returns the first
+ * error any item reported.  Every item is computed on its own, so the
+ * result does not depend on the thread count. */
+static int run_job(struct decode_job *jb) {
+  const int num_threads = jb->num_threads;
+  jb->status = OR_OK;
+  pthread_mutex_init(&jb->lock, NULL);
+  pthread_t *th = malloc(sizeof(pthread_t) * (size_t)num_threads);
+  struct worker_arg *wa = malloc(sizeof(struct worker_arg) * (size_t)num_threads);
+  if (!th || !wa) {
+    free(th);
+    free(wa);
+    pthread_mutex_destroy(&jb->lock);
+    return OR_ERR_NOMEM;
+  }
+  int started = 0;
+  for (int t = 0; t < num_threads; ++t) {
+    wa[t].jb = jb;
+    wa[t].tid = t;
+    if (pthread_create(&th[t], NULL, decode_worker, &wa[t]) != 0)
+      break;
+    ++started;
+  }
+  if (started == 0) { /* no thread could start: run the items here */
+    wa[0].jb = jb;
+    wa[0].tid = 0;
+    jb->num_threads = 1;
+    decode_worker(&wa[0]);
+  } else if (started < num_threads) {
+    /* items owned by threads that never started: run them here */
+    for (int t = started; t < num_threads; ++t)
+      decode_worker(&wa[t]);
+  }
+  for (int t = 0; t < started; ++t)
+    pthread_join(th[t], NULL);
+  free(th);
+  free(wa);
+  pthread_mutex_destroy(&jb->lock);
+  return jb->status;
 }
 
 /* out: double [num_items, head_dim].  Without `sel`, the items are every
@@ -408,41 +470,77 @@ int oracle_paged_decode_q(double *out, const void *q, const void *k_cache,
         return OR_ERR_ARG;
   }
   jb.num_threads = num_threads;
-  jb.status = OR_OK;
-  pthread_mutex_init(&jb.lock, NULL);
+  return run_job(&jb);
+}
 
-  pthread_t *th = malloc(sizeof(pthread_t) * (size_t)num_threads);
-  struct worker_arg *wa = malloc(sizeof(struct worker_arg) * (size_t)num_threads);
-  if (!th || !wa) {
-    free(th);
-    free(wa);
-    pthread_mutex_destroy(&jb.lock);
-    return OR_ERR_NOMEM;
+/* Multi-query attention for chunked prefill: a long prompt is processed
+ * in chunks ("Inside vLLM: How PagedAttention Eliminates KV-Cache Memory
+ * Waste", section "Continuous Batching and Chunked Prefill"), so each
+ * sequence brings a chunk of C_s new query tokens whose keys and values are
+ * already in its blocks.  Query rows of sequence s are
+ * query_start_loc[s] .. query_start_loc[s+1]-1 of q ([num_query_tokens,
+ * num_heads, head_dim]); they are the last C_s tokens of its
+ * context_lens[s] tokens, and each attends causally (see decode_worker).
+ * out: double [num_query_tokens, num_heads, head_dim], or one row per
+ * (query row, head) pair of `sel`.  Rejected: query_start_loc not starting
+ * at 0, decreasing, not ending at num_query_tokens, or a chunk longer than
+ * its context. */
+int oracle_paged_prefill(double *out, const void *q, const void *k_cache,
+                         const void *v_cache, const int32_t *block_tables,
+                         const int32_t *context_lens,
+                         const int32_t *query_start_loc, float scale,
+                         int block_size, int num_seqs, int64_t num_query_tokens,
+                         int num_heads, int num_kv_heads, int head_dim,
+                         int64_t num_blocks, int max_blocks_per_seq,
+                         int q_dtype, int cache_dtype, float k_scale,
+                         float v_scale, const int32_t *sel, int64_t num_sel,
+                         int num_threads) {
+  const int dtype = cache_dtype;
+  if (num_seqs < 0 || num_query_tokens < 0 || num_heads <= 0 ||
+      num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || head_dim <= 0 ||
+      block_size <= 0 || block_size % 4 != 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || dtype < OR_F32 || dtype > OR_FP8 ||
+      q_dtype < OR_F32 || q_dtype > OR_BF16 || num_threads <= 0 ||
+      !query_start_loc)
+    return OR_ERR_ARG;
+  if (query_start_loc[0] != 0 || query_start_loc[num_seqs] != num_query_tokens)
+    return OR_ERR_ARG;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t C = (int64_t)query_start_loc[s + 1] - query_start_loc[s];
+    if (C < 0 || C > context_lens[s])
+      return OR_ERR_ARG;
   }
-  int started = 0;
-  for (int t = 0; t < num_threads; ++t) {
-    wa[t].jb = &jb;
-    wa[t].tid = t;
-    if (pthread_create(&th[t], NULL, decode_worker, &wa[t]) != 0)
-      break;
-    ++started;
+  if (sel) {
+    for (int64_t i = 0; i < num_sel; ++i)
+      if (sel[2 * i] < 0 || sel[2 * i] >= num_query_tokens ||
+          sel[2 * i + 1] < 0 || sel[2 * i + 1] >= num_heads)
+        return OR_ERR_ARG;
   }
-  if (started == 0) { /* no thread could start: run the items here */
-    wa[0].jb = &jb;
-    wa[0].tid = 0;
-    jb.num_threads = 1;
-    decode_worker(&wa[0]);
-  } else if (started < num_threads) {
-    /* items owned by threads that never started: run them here */
-    for (int t = started; t < num_threads; ++t)
-      decode_worker(&wa[t]);
-  }
-  for (int t = 0; t < started; ++t)
-    pthread_join(th[t], NULL);
-  free(th);
-  free(wa);
-  pthread_mutex_destroy(&jb.lock);
-  return jb.status;
+  struct decode_job jb;
+  memset(&jb, 0, sizeof jb);
+  jb.out = out;
+  jb.q = q;
+  jb.k_cache = k_cache;
+  jb.v_cache = v_cache;
+  jb.block_tables = block_tables;
+  jb.context_lens = context_lens;
+  jb.query_start_loc = query_start_loc;
+  jb.scale = (double)scale;
+  jb.block_size = block_size;
+  jb.num_seqs = num_seqs;
+  jb.num_heads = num_heads;
+  jb.num_kv_heads = num_kv_heads;
+  jb.head_dim = head_dim;
+  jb.num_blocks = num_blocks;
+  jb.max_blocks_per_seq = max_blocks_per_seq;
+  jb.dtype = dtype;
+  jb.q_dtype = q_dtype;
+  jb.k_scale = (double)k_scale;
+  jb.v_scale = (double)v_scale;
+  jb.sel = sel;
+  jb.num_items = sel ? num_sel : num_query_tokens * num_heads;
+  jb.num_threads = num_threads;
+  return run_job(&jb);
 }
 
 /* q and caches of one type, no scaling. */

@@ -12,6 +12,7 @@ import pytest
 import oracle
 import test_oracle_blocks as blockpins
 import test_oracle_fp8 as fp8pins
+import test_oracle_prefill as prefillpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_oracle.c")
@@ -41,8 +42,8 @@ MUTANTS = {
     "fp16_exponent_bias": ("ex - 25);", "ex - 24);"),
     "bf16_wrong_half": ("uint32_t u = (uint32_t)b << 16;",
                         "uint32_t u = (uint32_t)b << 15;"),
-    "query_head_ignored": ("qbase = ((size_t)s * jb->num_heads + h) * hd;",
-                           "qbase = ((size_t)s * jb->num_heads) * hd;"),
+    "query_head_ignored": ("qbase = ((size_t)qrow * jb->num_heads + h) * hd;",
+                           "qbase = ((size_t)qrow * jb->num_heads) * hd;"),
     "e4m3_exponent_bias": ("ldexp((double)(8 + fr), ex - 10)",
                            "ldexp((double)(8 + fr), ex - 11)"),
     "e4m3_ties_to_odd": ("(a - vlo == vhi - a && (lo & 1))",
@@ -53,6 +54,12 @@ MUTANTS = {
     "copy_blocks_reversed": (
         "memcpy((char *)k_cache + d * bytes, (const char *)k_cache + s * bytes, bytes);",
         "memcpy((char *)k_cache + s * bytes, (const char *)k_cache + d * bytes, bytes);"),
+    "causal_excludes_self": (
+        "L = (int)(jb->context_lens[s] - C + (r - qsl[s]) + 1);",
+        "L = (int)(jb->context_lens[s] - C + (r - qsl[s]));"),
+    "chunk_at_the_start": (
+        "L = (int)(jb->context_lens[s] - C + (r - qsl[s]) + 1);",
+        "L = (int)((r - qsl[s]) + 1);"),
     "swap_values_from_keys": (
         "memcpy((char *)dst_v + d * bytes, (const char *)src_v + s * bytes, bytes);",
         "memcpy((char *)dst_v + d * bytes, (const char *)src_k + s * bytes, bytes);"),
@@ -82,6 +89,8 @@ def _pin_calls():
     calls += [lambda: blockpins.test_copy_blocks_is_row_assignment("f32", 12, 2, 16, 64, 5),
               lambda: blockpins.test_swap_blocks_is_row_assignment("bf16", 30, 10, 7),
               blockpins.test_swap_blocks_round_trip_and_rejections]
+    calls += [lambda c=c: prefillpins.test_matches_masked_contiguous_attention(c)
+              for c in (0, 2)]
     return calls
 
 

@@ -113,6 +113,44 @@ class Workload:
     new_rows: np.ndarray          # int64 [S]: row of token L-1 (the new token)
     refcount: np.ndarray          # int32 [num_blocks]: tables referencing a block
     meta: dict = field(default_factory=dict)
+    # multi-query (chunked prefill) workloads: q holds [T, Hq, D], one row
+    # per chunk token; sequence s's rows are query_start_loc[s] ..
+    # query_start_loc[s+1]-1, its last C_s tokens.  None for decode.
+    query_start_loc: np.ndarray | None = None   # int32 [S+1]
+
+    # -- chunked prefill: the chunk is the last C_s tokens of each sequence;
+    # the step writes the chunk's K/V, then attends (causally) for every
+    # chunk token.  The earlier context is written beforehand.
+    def chunk_lens(self) -> np.ndarray:
+        return np.diff(self.query_start_loc).astype(np.int64)
+
+    def chunk_rows(self) -> np.ndarray:
+        return np.concatenate(
+            [self.token_rows[s][len(self.token_rows[s]) - int(c):]
+             for s, c in enumerate(self.chunk_lens())] + [np.zeros(0, np.int64)])
+
+    def context_slots(self) -> np.ndarray:
+        """Slots of every row, the chunk rows marked -1 (no write)."""
+        s = self.kv_slots.copy()
+        s[self.chunk_rows()] = -1
+        return s
+
+    def chunk_k(self) -> np.ndarray:
+        return self.kv_k[self.chunk_rows()]
+
+    def chunk_v(self) -> np.ndarray:
+        return self.kv_v[self.chunk_rows()]
+
+    def chunk_slots(self) -> np.ndarray:
+        return self.kv_slots[self.chunk_rows()]
+
+    def attended_pairs(self) -> int:
+        """(query token, context token) pairs the causal chunks attend, per
+        query head: sum over chunk tokens of their position + 1."""
+        tot = 0
+        for L, C in zip(self.context_lens.astype(np.int64), self.chunk_lens()):
+            tot += int(C) * (int(L) - int(C)) + int(C) * (int(C) + 1) // 2
+        return tot
 
     # The decode step writes each sequence's newest token, then attends.
     # Prefill = every other row; its slot list marks the new rows with -1
@@ -177,12 +215,14 @@ def build(name: str, *, lens, num_heads: int, num_kv_heads: int,
           num_blocks=None, pool_factor: float = 1.0, max_blocks_per_seq=None,
           prefix_len: int = 0, key_outlier_frac: float = 0.0,
           key_outlier_mult: float = 8.0, scale=None, rng=None,
-          meta=None) -> Workload:
+          meta=None, chunk_lens=None) -> Workload:
     """Generic builder.  `lens` are the context lengths (new token
     included).  With prefix_len > 0 every sequence starts with the same
     prefix_len tokens held in shared blocks (prefix_len must be a multiple
     of block_size).  The generator `rng` must already have drawn `lens` if
-    the caller drew them from it (placement continues the same stream)."""
+    the caller drew them from it (placement continues the same stream).
+    With `chunk_lens` (C_s <= L_s per sequence) the workload is a chunked
+    prefill: q gets one row per chunk token."""
     rng = rng if rng is not None else np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     S = len(lens)
@@ -212,7 +252,14 @@ def build(name: str, *, lens, num_heads: int, num_kv_heads: int,
             np.arange(R, R + own, dtype=np.int64)]))
         R += own
     Hq, Hkv, D = num_heads, num_kv_heads, head_dim
-    q = normal(S * Hq * D, dtype, seed, _STREAM_Q).reshape(S, Hq, D)
+    qsl = None
+    if chunk_lens is not None:
+        chunk_lens = np.asarray(chunk_lens, np.int64)
+        assert chunk_lens.shape == (S,) and np.all(chunk_lens >= 0)
+        assert np.all(chunk_lens <= lens)
+        qsl = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    T = S if qsl is None else int(qsl[-1])
+    q = normal(T * Hq * D, dtype, seed, _STREAM_Q).reshape(T, Hq, D)
     kk = normal(R * Hkv * D, dtype, seed, _STREAM_K).reshape(R, Hkv, D)
     vv = normal(R * Hkv * D, dtype, seed, _STREAM_V).reshape(R, Hkv, D)
 
@@ -244,7 +291,8 @@ def build(name: str, *, lens, num_heads: int, num_kv_heads: int,
                     context_lens=lens.astype(np.int32), block_tables=bt,
                     q=q, kv_k=kk, kv_v=vv, kv_slots=slots,
                     token_rows=rows_per_seq, new_rows=new_rows,
-                    refcount=refcount, meta=dict(meta or {}, seed=seed))
+                    refcount=refcount, meta=dict(meta or {}, seed=seed),
+                    query_start_loc=qsl)
 
 
 # ----------------------------------------------------- the named configs ----
@@ -316,6 +364,52 @@ def shared_prefix(seed: int = 0, block_size: int = 16,
                  max_blocks_per_seq=(1024 + 512) // block_size, rng=rng)
 
 
+def prefill70b(seed: int = 0, num_seqs: int = 16, chunk: int = 512) -> Workload:
+    """Chunked prefill, 70B-class grouped-query layer: 16 sequences, each
+    bringing a chunk of 512 prompt tokens after an earlier context uniform
+    on [0, 3584] tokens; 64 query heads over 8 KV heads, head_dim 128,
+    bf16, 16-token blocks at random places in an exactly sized pool."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, 3584, size=num_seqs, endpoint=True)
+    lens = prior + chunk
+    return build("prefill70b", lens=lens, num_heads=64, num_kv_heads=8,
+                 head_dim=128, block_size=16, dtype="bf16", seed=seed,
+                 max_blocks_per_seq=(3584 + chunk) // 16, rng=rng,
+                 chunk_lens=[chunk] * num_seqs)
+
+
+def prefill13b(seed: int = 0, num_seqs: int = 8, chunk: int = 512) -> Workload:
+    """Chunked prefill, 13B-class multi-head layer: 8 sequences, chunks of
+    512 tokens after an earlier context uniform on [0, 1536]; 40 heads,
+    head_dim 128, fp16, 16-token blocks, a pool twice the blocks needed."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, 1536, size=num_seqs, endpoint=True)
+    lens = prior + chunk
+    return build("prefill13b", lens=lens, num_heads=40, num_kv_heads=40,
+                 head_dim=128, block_size=16, dtype="f16", seed=seed,
+                 pool_factor=2.0, max_blocks_per_seq=(1536 + chunk) // 16,
+                 rng=rng, chunk_lens=[chunk] * num_seqs)
+
+
+def random_prefill_case(seed: int, *, num_seqs: int, max_prior: int,
+                        max_chunk: int, num_heads: int, num_kv_heads: int,
+                        head_dim: int, block_size: int, dtype: str,
+                        pool_factor: float = 1.5) -> Workload:
+    """A small random chunked-prefill case: earlier context uniform on
+    [0, max_prior], chunk uniform on [0, max_chunk] (zero allowed: that
+    sequence has no query rows)."""
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, max_prior, size=num_seqs, endpoint=True)
+    chunk = rng.integers(0, max_chunk, size=num_seqs, endpoint=True)
+    lens = prior + chunk
+    return build(f"prefill_random{seed}", lens=lens, num_heads=num_heads,
+                 num_kv_heads=num_kv_heads, head_dim=head_dim,
+                 block_size=block_size, dtype=dtype, seed=seed,
+                 pool_factor=pool_factor, rng=rng, chunk_lens=chunk,
+                 max_blocks_per_seq=max(1, -(-(max_prior + max_chunk)
+                                             // block_size)))
+
+
 CONFIGS = {
     "tiny": tiny,
     "mha13b": mha13b,
@@ -323,6 +417,11 @@ CONFIGS = {
     "long_split": long_split,
     "shared_prefix_bs16": lambda seed=0: shared_prefix(seed, 16),
     "shared_prefix_bs32": lambda seed=0: shared_prefix(seed, 32),
+}
+
+PREFILL_CONFIGS = {
+    "prefill70b": prefill70b,
+    "prefill13b": prefill13b,
 }
 
 
