@@ -49,9 +49,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="mha13b",
+    p.add_argument("--workload", default=None,
                    choices=["tiny", "mha13b", "gqa70b", "long_split",
-                            "shared_prefix_bs16", "shared_prefix_bs32"])
+                            "shared_prefix_bs16", "shared_prefix_bs32",
+                            "prefill70b", "prefill13b"],
+                   help="default: mha13b (decode), prefill70b (prefill)")
     p.add_argument("--variant", default="single", choices=["single", "split"])
     p.add_argument("--partition", type=int, default=512)
     p.add_argument("--kv-dtype", default="same", choices=["same", "fp8"],
@@ -60,10 +62,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--mode", default="decode",
-                   choices=["decode", "copy_blocks", "swap"],
+                   choices=["decode", "copy_blocks", "swap", "prefill"],
                    help="decode: the decode step (default); copy_blocks: the "
                         "copy-on-write block copy; swap: blocks out to pinned "
-                        "host memory and back")
+                        "host memory and back; prefill: chunked-prefill "
+                        "attention (--workload prefill70b|prefill13b)")
     p.add_argument("--pairs", type=int, default=2048,
                    help="copy_blocks mode: block pairs copied per launch")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -115,6 +118,11 @@ def main():
         return bench_copy_blocks(args)
     if args.mode == "swap":
         return bench_swap(args)
+    if args.mode == "prefill":
+        return bench_prefill(args)
+    args.workload = args.workload or "mha13b"
+    if args.workload not in wl.CONFIGS:
+        raise SystemExit(f"{args.workload} is a prefill workload: use --mode prefill")
     t0 = time.time()
     w = wl.CONFIGS[args.workload](args.seed)
     log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_heads} "
@@ -324,6 +332,156 @@ def bench_copy_blocks(args):
 
 
 HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense, no sparsity
+
+
+def bench_prefill(args):
+    """Chunked prefill: every sequence brings a chunk of prompt tokens; the
+    step writes the chunk's K/V (reshape_and_cache) and then runs
+    paged_attention_prefill for every chunk token (causal).  Work is counted
+    as 4 * head_dim flops per (query token, query head, attended token)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_309_amd as pkv
+    import workloads as wl
+
+    name = args.workload or "prefill70b"
+    if name not in wl.PREFILL_CONFIGS:
+        raise SystemExit(f"{name} is not a prefill workload")
+    t0 = time.time()
+    w = wl.PREFILL_CONFIGS[name](args.seed)
+    T = w.q.shape[0]
+    log(f"[bench] workload {w.name}: S={w.num_seqs} T={T} Hq={w.num_heads} "
+        f"Hkv={w.num_kv_heads} D={w.head_dim} dtype={w.dtype} "
+        f"generated in {time.time()-t0:.1f}s")
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    kc, vc = pkv.new_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size,
+                              w.head_dim, tdt, fill=0.0)
+    pkv.reshape_and_cache(dev(w.kv_k), dev(w.kv_v), kc, vc,
+                          torch.from_numpy(w.context_slots()).cuda())
+    ck, cv = dev(w.chunk_k()), dev(w.chunk_v())
+    cslots = torch.from_numpy(w.chunk_slots()).cuda()
+    q = dev(w.q)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).cuda()
+    cl = torch.from_numpy(w.context_lens).cuda()
+    qsl = torch.from_numpy(w.query_start_loc).cuda()
+    mq = int(w.chunk_lens().max())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+        pkv.reshape_and_cache(ck, cv, kc, vc, cslots)
+        if record:
+            e[1].record(stream)
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, w.scale,
+                                    max_query_len=mq)
+        if record:
+            e[2].record(stream)
+            ev.append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / args.steps
+    att_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    rac_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    calibration_copy(args.calib_copy_mib)
+    flops = 4.0 * w.head_dim * w.num_heads * w.attended_pairs()
+    att_mean = float(np.mean(att_ms))
+    achieved = flops / (att_mean * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    tok_s = T / (ms_step * 1e-3)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(w, flops)
+    rec = {"metric": "chunked-prefill attention TFLOP/s (causal, "
+                     "4*head_dim flops per attended (token, head, key)) + "
+                     "prefill tokens/s",
+           "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "num_seqs": w.num_seqs,
+                      "query_tokens": T, "num_heads": w.num_heads,
+                      "num_kv_heads": w.num_kv_heads,
+                      "head_dim": w.head_dim, "block_size": w.block_size,
+                      "num_blocks": w.num_blocks, "seed": args.seed,
+                      "chunk": mq,
+                      "mean_context": float(w.context_lens.mean()),
+                      "attended_pairs_per_head": w.attended_pairs(),
+                      "accumulate": "f32"},
+           "prefill_tokens_per_s": round(tok_s, 1),
+           "kernels_ms": {"reshape_and_cache": round(float(np.mean(rac_ms)), 5),
+                          "attention": round(att_mean, 5),
+                          "attention_p10": round(float(np.percentile(att_ms, 10)), 5),
+                          "attention_p90": round(float(np.percentile(att_ms, 90)), 5)},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                        "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4),
+                        "traffic": stored_traffic("prefill_mfma_kernel", w.name),
+                        "kernel": "prefill_mfma_kernel",
+                        "algorithmic_flops_per_launch": flops,
+                        "mean_launch_ms": round(att_mean, 5)},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_prefill(w, flops_total, sample_rows=512):
+    """The oracle on a bounded sample: every query head of `sample_rows`
+    chunk tokens spread over the batch; flop rate scaled by the sampled
+    tokens' share of the work."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    kc, vc = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
+                             w.head_dim, w.dtype, fill="zero")
+    oracle.reshape_and_cache(w.kv_k, w.kv_v, kc, vc, w.kv_slots,
+                             w.num_kv_heads, w.head_dim, w.block_size,
+                             w.num_blocks, w.dtype)
+    T = w.q.shape[0]
+    rows = np.linspace(0, T - 1, sample_rows).astype(np.int64)
+    sel = np.stack([np.repeat(rows, w.num_heads),
+                    np.tile(np.arange(w.num_heads), rows.size)], 1).astype(np.int32)
+    # attended tokens of each sampled row
+    qsl = w.query_start_loc
+    seq = np.searchsorted(qsl, rows, side="right") - 1
+    pos = w.context_lens[seq].astype(np.int64) - np.diff(qsl)[seq] + (rows - qsl[seq])
+    flops = 4.0 * w.head_dim * w.num_heads * float(np.sum(pos + 1))
+    t1 = time.perf_counter()
+    out = oracle.paged_prefill(w.q, kc, vc, w.block_tables, w.context_lens,
+                               qsl, w.scale, w.block_size, w.num_kv_heads,
+                               w.num_blocks, w.dtype, sel=sel, threads=threads)
+    dt = time.perf_counter() - t1
+    assert np.all(np.isfinite(out))
+    log(f"[bench] oracle sample {dt:.2f}s")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{sample_rows} chunk tokens x {w.num_heads} heads of "
+                      f"{w.name} ({flops / flops_total:.4f} of the step's "
+                      f"attention work)"}
 
 
 def bench_swap(args):

@@ -196,6 +196,43 @@ int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
                                  void *workspace, size_t workspace_bytes,
                                  const pkv_dims *dims, pkv_stream_t stream);
 
+/*
+ * paged_attention_prefill - multi-query attention over the paged cache for
+ * chunked prefill.
+ *
+ * A long prompt is processed in chunks interleaved with decode steps
+ * ("Inside vLLM: How PagedAttention Eliminates KV-Cache Memory Waste",
+ * section "Continuous Batching and Chunked Prefill").  Before this call the
+ * chunk's keys and values are written with reshape_and_cache, so sequence s
+ * holds context_lens[s] tokens of which its chunk is the last
+ * C_s = query_start_loc[s+1] - query_start_loc[s].  Chunk token j (row
+ * query_start_loc[s] + j of q) sits at position context_lens[s] - C_s + j
+ * and attends, through the block table, to every token up to and including
+ * itself (causal within the chunk); the result is ordinary attention over
+ * that prefix ("PagedAttention: how vLLM manages the KV cache", section
+ * "PagedAttention changes addressing inside attention").  A one-token chunk
+ * is a decode step.
+ *
+ *   out, q            [num_query_tokens, num_heads, head_dim], dims->dtype
+ *   query_start_loc   int32 [num_seqs + 1]: 0 = start[0] <= ... <=
+ *                     start[num_seqs] = num_query_tokens (device)
+ *   max_query_len     an upper bound of every C_s (host-side; sizes the grid)
+ *   k_cache, v_cache, block_tables, context_lens: as for decode.
+ * dims->dtype must be PKV_F16 or PKV_BF16 (the matrix-core kernel; fp32
+ * returns PKV_ERR_DTYPE).  Probabilities enter the value product rounded to
+ * dims->dtype, accumulation is fp32.  Preconditions (device data, not
+ * checked): C_s <= max_query_len and C_s <= context_lens[s]; rows of a
+ * query token whose position would be negative are written as zeros.
+ * Asynchronous on `stream`; returns a pkv_status.
+ */
+int paged_attention_prefill(void *out, const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *block_tables,
+                            const int32_t *context_lens,
+                            const int32_t *query_start_loc, float scale,
+                            int block_size, int num_query_tokens,
+                            int max_query_len, const pkv_dims *dims,
+                            pkv_stream_t stream);
+
 /* ---- 8-bit (E4M3) caches ----------------------------------------------
  * Lower-precision cache formats reduce the bytes per element ("PagedAttention:
  * how vLLM manages the KV cache", section "Keep the tensor formula beside the

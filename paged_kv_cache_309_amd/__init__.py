@@ -24,8 +24,8 @@ from ._lib import PkvDims, PkvError
 
 __all__ = ["reshape_and_cache", "paged_attention_decode",
            "paged_attention_decode_split", "split_workspace_bytes",
-           "new_kv_cache", "copy_blocks", "swap_blocks", "BlockManager",
-           "PkvError", "version"]
+           "paged_attention_prefill", "new_kv_cache", "copy_blocks",
+           "swap_blocks", "BlockManager", "PkvError", "version"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
            torch.bfloat16: _lib.PKV_BF16}
@@ -162,6 +162,32 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), bs, int(partition_size),
         _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(dims), _stream(stream)))
+    return out
+
+
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor,
+                            context_lens: torch.Tensor,
+                            query_start_loc: torch.Tensor, scale: float,
+                            max_query_len: int | None = None,
+                            block_size: int | None = None,
+                            stream=None) -> torch.Tensor:
+    """Chunked prefill: q / out [T, Hq, D] hold the chunk tokens of every
+    sequence (rows query_start_loc[s] .. query_start_loc[s+1]-1, the last
+    tokens of its context, whose K/V are already in the cache); each
+    attends causally.  max_query_len bounds every chunk (default T)."""
+    T = q.shape[0]
+    bs = block_size or k_cache.shape[2]
+    S = context_lens.shape[0]
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    dims = PkvDims(S, q.shape[1], Hkv, q.shape[2], NB, block_tables.shape[1],
+                   _dtype(q))
+    mq = T if max_query_len is None else int(max_query_len)
+    _lib.check(_lib.lib().paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start_loc), float(scale), bs, T, mq,
         ctypes.byref(dims), _stream(stream)))
     return out
 

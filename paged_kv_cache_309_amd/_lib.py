@@ -34,7 +34,8 @@ EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_bm_num_tokens",
            "swap_blocks", "pkv_bm_create_with_host", "pkv_bm_swap_out",
            "pkv_bm_swap_in", "pkv_bm_num_free_host_blocks",
-           "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table")
+           "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table",
+           "paged_attention_prefill")
 
 
 class PkvDims(ctypes.Structure):
@@ -102,6 +103,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_bm_refcount.argtypes = [P, I32]
     lib.pkv_bm_num_tokens.restype = I32
     lib.pkv_bm_num_tokens.argtypes = [P, I64]
+    lib.paged_attention_prefill.restype = I
+    lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P,
+                                            ctypes.c_float, I, I, I, D, P]
     lib.swap_blocks.restype = I
     lib.swap_blocks.argtypes = [P, P, P, P, P, I, I32, I32, I, D, P]
     lib.pkv_bm_create_with_host.restype = I

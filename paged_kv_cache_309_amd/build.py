@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "decode_vector.hip", "decode_mfma.hip",
-           "reduce_and_cache.hip", "copy_blocks.hip", "block_manager.cpp"]
+           "prefill_mfma.hip", "reduce_and_cache.hip", "copy_blocks.hip",
+           "block_manager.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

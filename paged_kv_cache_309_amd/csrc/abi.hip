@@ -226,6 +226,65 @@ int decode(void *out, const void *q, const void *k_cache, const void *v_cache,
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+            const int32_t *block_tables, const int32_t *context_lens,
+            const int32_t *query_start_loc, float scale, int block_size, int num_query_tokens,
+            int max_query_len, const pkv_dims *dims, pkv_stream_t stream, int cache_dtype,
+            float k_scale, float v_scale) {
+  size_t sb = 0, cb = 0;
+  int rc = check_decode(dims, block_size, &sb, &cb, cache_dtype == kCacheSame ? 0 : 1);
+  if (rc != PKV_OK) return rc;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
+  // the matrix-core kernel takes 16-bit queries and caches
+  if (dims->dtype == PKV_F32 || cache_dtype != kCacheSame) return PKV_ERR_DTYPE;
+  if (num_query_tokens < 0 || max_query_len < 0) return PKV_ERR_SHAPE;
+  const int G = dims->num_heads / dims->num_kv_heads;
+  const u128 qb = (u128)num_query_tokens * (u128)dims->num_heads * (u128)dims->head_dim *
+                  (u128)elem_bytes(dims->dtype);
+  if (qb > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  // no chunk is longer than all query tokens together
+  const int64_t rows = (int64_t)(max_query_len < num_query_tokens ? max_query_len
+                                                                  : num_query_tokens) * G;
+  const int64_t rpw = pkv::prefill_rows_per_workgroup();
+  const int64_t q_blocks = (rows + rpw - 1) / rpw;
+  if (q_blocks > kMaxGridYZ) return PKV_ERR_SHAPE;
+  if (dims->num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start_loc, 4))
+    return PKV_ERR_ALIGN;
+  const size_t tb = (size_t)dims->num_seqs * (size_t)dims->max_blocks_per_seq * 4;
+  const size_t lb = (size_t)dims->num_seqs * 4;
+  const size_t ob = (size_t)qb;
+  if (overlap(out, ob, q, ob) || overlap(out, ob, k_cache, cb) || overlap(out, ob, v_cache, cb) ||
+      overlap(out, ob, block_tables, tb) || overlap(out, ob, context_lens, lb) ||
+      overlap(out, ob, query_start_loc, lb + 4))
+    return PKV_ERR_ALIAS;
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634074);
+  a.v_scale = v_scale;
+  a.num_seqs = dims->num_seqs;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.num_blocks = dims->num_blocks;
+  a.max_blocks = dims->num_blocks > 0 ? dims->max_blocks_per_seq : 0;
+  a.num_query_tokens = num_query_tokens;
+  a.q_blocks = (int)q_blocks;
+  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
+  const hipError_t err =
+      pkv::launch_prefill_mfma(a, dims->dtype, ct, dims->head_dim, block_size, max_query_len,
+                               reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
 int decode_split(void *out, const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *block_tables, const int32_t *context_lens, float scale,
                  int block_size, int partition_size, void *workspace,
@@ -307,6 +366,16 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
                                const pkv_dims *dims, pkv_stream_t stream) {
   return decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                 dims, stream, pkv::DT_FP8, k_scale, v_scale);
+}
+
+int paged_attention_prefill(void *out, const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *block_tables,
+                            const int32_t *context_lens, const int32_t *query_start_loc,
+                            float scale, int block_size, int num_query_tokens,
+                            int max_query_len, const pkv_dims *dims, pkv_stream_t stream) {
+  return prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                 block_size, num_query_tokens, max_query_len, dims, stream, kCacheSame, 1.f,
+                 1.f);
 }
 
 int paged_attention_split_workspace_bytes(const pkv_dims *dims, int block_size,

@@ -32,79 +32,9 @@
 // The probabilities enter the value product as a high and a low
 // half-precision part (p = hi + lo to about 16 significant bits), so the
 // weights keep near-fp32 precision.
-#include "pkv_device.h"
+#include "mfma_ops.h"
 
 namespace pkv {
-
-template <int DT> struct MfmaOps;
-
-template <> struct MfmaOps<DT_BF16> {
-  __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        __builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-  }
-  // two probabilities -> packed (hi, lo) bfloat16 pairs with hi + lo ~= p:
-  // hi keeps the top 16 bits of p, lo the top 16 bits of the remainder
-  __device__ static __forceinline__ void split2(float p0, float p1, uint32_t &hi,
-                                                uint32_t &lo) {
-    const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
-    const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-    const uint32_t r0 = __float_as_uint(p0 - __uint_as_float(h0));
-    const uint32_t r1 = __float_as_uint(p1 - __uint_as_float(h1));
-    hi = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
-    lo = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
-  }
-};
-
-template <> struct MfmaOps<DT_F16> {
-  __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
-        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(
-        __builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ void split2(float p0, float p1, uint32_t &hi,
-                                                uint32_t &lo) {
-    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-    const f16x2 r = __builtin_bit_cast(
-        f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - static_cast<float>(h.x),
-                                          p1 - static_cast<float>(h.y)));
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, r);
-  }
-};
-
-// One 16-token tile as loaded: 16-byte chunks of K and of V per lane.
-// 16-bit caches: chunk kk of K is the A operand of logit MFMA kk, chunk u of
-// V holds the A operands of value n-tiles 2u and 2u+1.  8-bit caches: chunk
-// cp of K holds logit MFMAs 2cp and 2cp+1, chunk u of V holds n-tiles
-// 4u .. 4u+3; they are widened to 16 bits in registers.
-template <int CT, int D>
-struct MfmaTile {
-  static constexpr int NC = CT == DT_FP8 ? D / 64 : D / 32;
-  u32x4 k[NC];
-  u32x4 v[NC];
-};
-
-// Two E4M3 bytes -> two 16-bit operands of type OT, exactly (every E4M3
-// value is a bfloat16 and a binary16 value).
-template <int OT>
-__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w, bool hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
-                     : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-  if constexpr (OT == DT_BF16) {
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
-  }
-}
 
 // QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
 template <int QT, int CT, int D, int BS, bool SPLIT>

@@ -188,8 +188,9 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
 
 // Walks the 16-token tiles a wavefront owns, with one tile of prefetch.
 //
-// The wave owns tiles k = k0 + 4n, n = 0 .. n_mine-1 (k0 = first tile of the
-// range + wave index); tile k lives in block table entry k / subs, at token
+// The wave owns tiles k = k0 + STRIDE*n, n = 0 .. n_mine-1 (decode: k0 =
+// first tile of the range + wave index, STRIDE = 4 waves; prefill: every
+// tile, STRIDE = 1); tile k lives in block table entry k / subs, at token
 // offset 16 * (k % subs) of that block.  Block-table entries are fetched
 // 64 at a time, one per lane, and broadcast with readlane, so the byte
 // offset of every tile is a wave-uniform (scalar) value.
@@ -198,7 +199,7 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
 //   compute(tile, n)         consumes the n-th tile
 //
 // Two tile buffers alternate (no register copies between iterations).
-template <class Tile, class Load, class Compute>
+template <class Tile, int STRIDE = 4, class Load, class Compute>
 __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mine,
                                            int subs, unsigned num_blocks,
                                            size_t head_off_bytes,
@@ -207,7 +208,7 @@ __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mi
   const int lane = threadIdx.x & 63;
   auto fetch = [&](int n0) -> int {
     const int n = n0 + lane;
-    return n < n_mine ? trow[(k0 + 4 * n) / subs] : 0;
+    return n < n_mine ? trow[(k0 + STRIDE * n) / subs] : 0;
   };
   int ent_cur = fetch(0);
   int ent_nxt = n_mine > 64 ? fetch(64) : 0;
@@ -218,7 +219,7 @@ __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mi
     }
     int phys = __builtin_amdgcn_readlane(ent_cur, n & 63);
     phys = (unsigned)phys < num_blocks ? phys : 0;
-    const int k = k0 + 4 * n;
+    const int k = k0 + STRIDE * n;
     return (size_t)phys * block_bytes + head_off_bytes + (size_t)(k % subs) * sub_bytes;
   };
   Tile ta, tb;

@@ -62,6 +62,28 @@ struct CopyBlocksArgs {
   int dst_num_blocks;
 };
 
+// Multi-query (chunked prefill) attention: query rows of sequence s are
+// query_start_loc[s] .. query_start_loc[s+1]-1 of q / out, the last C_s of
+// its context_lens[s] tokens, attending causally.
+struct PrefillArgs {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start_loc;
+  float scale_log2;  // scale * k_scale * log2(e)
+  float v_scale;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int max_blocks;
+  int num_query_tokens;
+  int q_blocks;      // grid extent over the query rows of one (seq, KV head)
+};
+
 // Each returns the launch error (hipSuccess when enqueued).
 // dtype: of q and out; cache_dtype: of the two pools (dtype, or DT_FP8)
 hipError_t launch_decode_vector(const DecodeArgs &a, int dtype, int cache_dtype,
@@ -75,6 +97,11 @@ hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
 hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
                                     int cache_dtype, int head_dim,
                                     int block_size, hipStream_t st);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
+                               int head_dim, int block_size, int max_query_len,
+                               hipStream_t st);
+// rows of one (sequence, KV head) a prefill workgroup covers
+int prefill_rows_per_workgroup();
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, int num_pairs,
                               hipStream_t st);
 
