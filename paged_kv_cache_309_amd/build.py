@@ -78,7 +78,9 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: a symbol no object defines is a link error, not a load error
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs",
+           "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

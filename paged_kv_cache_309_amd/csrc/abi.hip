@@ -247,7 +247,9 @@ int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                                                                   : num_query_tokens) * G;
   const int64_t rpw = pkv::prefill_rows_per_workgroup();
   const int64_t q_blocks = (rows + rpw - 1) / rpw;
-  if (q_blocks > kMaxGridYZ) return PKV_ERR_SHAPE;
+  if (q_blocks > INT_MAX ||
+      pkv::prefill_grid(dims->num_seqs, dims->num_kv_heads, (int)q_blocks) > INT_MAX)
+    return PKV_ERR_SHAPE;
   if (dims->num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return PKV_ERR_NULL;

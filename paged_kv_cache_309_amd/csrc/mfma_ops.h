@@ -15,6 +15,17 @@ template <> struct MfmaOps<DT_BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
         __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  // the same 16x16x32 product with the values as A over 32 tokens
+  __device__ static __forceinline__ f32x4 pv32(u32x4 a, u32x4 b, f32x4 c) {
+    return qk(a, b, c);
+  }
+  // two floats -> packed bfloat16 pair, nearest even (one instruction on
+  // gfx950)
+  __device__ static __forceinline__ uint32_t pack2(float p0, float p1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
+  }
   __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
         __builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
@@ -46,6 +57,13 @@ template <> struct MfmaOps<DT_F16> {
   __device__ static __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(
         __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 pv32(u32x4 a, u32x4 b, f32x4 c) {
+    return qk(a, b, c);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float p0, float p1) {
+    const f16x2 h = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};  // nearest even
+    return __builtin_bit_cast(uint32_t, h);
   }
   __device__ static __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(

@@ -100,8 +100,10 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
                                int head_dim, int block_size, int max_query_len,
                                hipStream_t st);
-// rows of one (sequence, KV head) a prefill workgroup covers
+// rows of one (sequence, KV head) a prefill workgroup covers, and the
+// number of workgroups a prefill launch takes
 int prefill_rows_per_workgroup();
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int q_blocks);
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, int num_pairs,
                               hipStream_t st);
 

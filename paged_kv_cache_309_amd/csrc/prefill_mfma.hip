@@ -12,20 +12,40 @@
 // changes addressing inside attention"); the chunk turns it into dense
 // products, so it runs on the matrix cores.
 //
-// The query rows of one (sequence, KV head) are the chunk's tokens times the
-// G query heads of the group, row r = token (r / G), head (r % G).  A
-// wavefront owns NQ tiles of 16 rows and walks every 16-token K/V tile its
-// rows can see, in order; per tile and row tile it issues D/32
-// v_mfma_f32_16x16x32 for S^T = K . Q^T and D/16 v_mfma_f32_16x16x16 for
-// O^T += V^T . P^T, with the lane layouts of the decode kernel (the logits
-// come out where the value product wants its B operand).  The K/V operands
-// of a tile are loaded once per wavefront and used by all its row tiles.
-// Tiles entirely before the wave's first query token need no mask; the
-// others mask every logit whose token lies after the row's own position.
+// Work: the query rows of one (sequence, KV head) are the chunk's tokens
+// times the G query heads of the group, row r = token (r / G), head (r % G).
+// A workgroup (4 wavefronts) takes 128 consecutive rows, each wavefront 32
+// of them (two row tiles of 16).  The workgroup walks the K/V of the
+// sequence in 32-token super-tiles through the block table: the four
+// wavefronts copy a super-tile (two 16-token tiles of K and of V) from HBM
+// into a ring of LDS stages with direct global-to-LDS loads, three
+// super-tiles ahead of the one being computed, and every wavefront takes
+// its matrix-core operands from there.  Per super-tile and row tile a wavefront issues 2 x D/32
+// v_mfma_f32_16x16x32 for S^T = K . Q^T (one per 16-token tile and 32 dims)
+// and D/16 v_mfma_f32_16x16x32 for O^T += V^T . P^T contracting over all 32
+// tokens.  Only tiles that reach past a wavefront's first query token are
+// masked (logits of tokens after the row's own position set to -inf).
 //
-// Probabilities enter the value product rounded once to the 16-bit type of
-// q (nearest even), and the running sum adds the same rounded values, so
-// the normalisation matches the weights actually applied.
+// Lane layouts: S^T of one 16-token tile comes out as lane l holding tokens
+// 4*(l/16)+i of row l%16.  The value product's contraction index k (32
+// tokens) is ordered so that lane l's eight B-operand slots k = 8*(l/16)+e
+// are those tokens of the first tile (e < 4) and of the second (e >= 4):
+// the probabilities stay in the lanes that computed them.  Its A operand
+// (V^T: dim rows, token columns) then needs, per lane, four consecutive
+// tokens of one dim from each tile, which the token-grouped V layout stores
+// as 8 contiguous bytes; dims 32u + 2m + j (j = 0, 1) make it one 16-byte
+// LDS read per tile for two n-tiles.  K rows are stored with their 16-byte
+// chunks permuted (see PrefillRing) so that lanes reading different token
+// rows use different banks.
+//
+// Scheduling: workgroup i runs on XCD i % 8.  All row blocks of one
+// (sequence, KV head) are given consecutive workgroup numbers on one XCD,
+// latest rows (longest prefixes) first, so the sequence's K/V stay in that
+// XCD's L2 while its row blocks run.
+//
+// Probabilities enter the value product rounded to the 16-bit type of q
+// (nearest even, one packed conversion per pair); the running sums add the
+// fp32 values; accumulation is fp32.
 #include "mfma_ops.h"
 
 namespace pkv {
@@ -34,23 +54,79 @@ constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillNQ = 2;  // 16-row query tiles per wavefront
 constexpr int kPrefillRows = kPrefillWaves * kPrefillNQ * 16;
+constexpr int kXcds = 8;
 
 int prefill_rows_per_workgroup() { return kPrefillRows; }
+
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int q_blocks) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  return (int64_t)kXcds * ((pairs + kXcds - 1) / kXcds) * q_blocks;
+}
+
+// LDS ring of super-tiles.  One super-tile is four 16-token pieces: K of
+// tile 0, K of tile 1, V of tile 0, V of tile 1, each 16 * D * 2 bytes and
+// each filled by one wavefront with direct global-to-LDS loads (64 lanes x
+// 16 bytes per instruction, lane i writing bytes 16i .. 16i+15 of its
+// 1 KiB block).  V pieces keep the HBM layout.  K pieces are stored with
+// the 16-byte chunks of each token row permuted: physical chunk p of row r
+// holds logical chunk p ^ (r % CR) (CR = chunks per row), so that the 16
+// lanes reading the same logical chunk of 16 different rows hit different
+// LDS banks.  The permutation is applied through the global address each
+// lane loads from.
+template <int D>
+struct PrefillRing {
+  static constexpr int PIECE = 16 * D * 2;
+  static constexpr int TILE = 4 * PIECE;
+  static constexpr int STAGES = 4;
+  static constexpr int CR = 2 * D / 16;  // 16-byte chunks per K row
+  static constexpr int LOADS = PIECE / 1024;  // per wavefront and super-tile
+};
+
+__device__ __forceinline__ u32x4 lds16(const char *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// One direct global-to-LDS load: 16 bytes per lane from `src`, written to
+// lds_base + 16 * lane.  The builtin only exists for the device; the host
+// pass of this single-source file sees an empty body.
+__device__ __forceinline__ void load_lds16(const char *src, char *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds_base;
+#endif
+}
+
+// Wait until at most n of this wavefront's vector-memory operations are
+// outstanding (n < 16; expcnt and lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
 
 template <int QT, int D, int BS>
 __global__ void __launch_bounds__(kPrefillThreads)
 prefill_mfma_kernel(PrefillArgs a) {
   using Ops = MfmaOps<QT>;
-  using Tl = MfmaTile<QT, D>;
-  constexpr int E = 2;        // cache element bytes
-  constexpr int KC = D / 32;  // logit MFMAs per tile and row tile
-  constexpr int NT = D / 16;  // value n-tiles
+  using RG = PrefillRing<D>;
+  constexpr int KC = D / 32;   // logit MFMAs per 16-token tile and row tile
+  constexpr int NC = D / 32;   // 16-byte V reads per lane and tile
+  constexpr int NT = D / 16;   // value n-tiles
   constexpr int NQ = kPrefillNQ;
+  constexpr int S = RG::STAGES;
+  __shared__ __attribute__((aligned(1024))) char ring[S * RG::TILE];
 
-  const int g = blockIdx.x, s = blockIdx.y;
-  const int blk = a.q_blocks - 1 - (int)blockIdx.z;  // latest rows (longest prefixes) first
-  const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads;
   const int G = Hq / Hkv;
+  const int wgi = blockIdx.x;
+  const int xcd = wgi % kXcds, nth = wgi / kXcds;
+  const int pair = (nth / a.q_blocks) * kXcds + xcd;
+  if (pair >= a.num_seqs * Hkv) return;  // the whole workgroup
+  const int blk = a.q_blocks - 1 - nth % a.q_blocks;
+  const int s = pair / Hkv, g = pair % Hkv;
+
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -61,17 +137,20 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int C = q1 - q0;
   const int L = max(0, min(a.context_lens[s], a.max_blocks * BS));
   const int R = C * G;
-  const int row0 = blk * kPrefillRows + w * NQ * 16;
-  if (row0 >= R) return;
-  const int row_last = min(row0 + NQ * 16, R) - 1;
-  const int pos_first = L - C + row0 / G;  // rows ascend with positions
-  const int pos_last = L - C + row_last / G;
-  const int kv_end = min(L, pos_last + 1);
-  const int n_tiles = kv_end > 0 ? (kv_end + 15) >> 4 : 0;
-  const int k_full = pos_first >= 0 ? (pos_first + 1) >> 4 : 0;  // tiles visible to every row
+  const int wg_row0 = blk * kPrefillRows;
+  if (wg_row0 >= R) return;  // the whole workgroup
+  const int wg_row_last = min(wg_row0 + kPrefillRows, R) - 1;
+  const int wg_kv_end = min(L, L - C + wg_row_last / G + 1);
+  const int n_super = wg_kv_end > 0 ? (wg_kv_end + 31) >> 5 : 0;
 
-  // this lane's row of each row tile: its position (-1: no row) and its
-  // Q^T operand (dims (kk*4 + grp)*8 .. +7 for logit MFMA kk)
+  // this wavefront's rows
+  const int row0 = wg_row0 + w * NQ * 16;
+  const bool has_rows = row0 <= wg_row_last;
+  const int row_last = min(row0 + NQ * 16 - 1, wg_row_last);
+  const int pos_first = L - C + row0 / G;  // rows ascend with positions
+  const int kv_end_w = has_rows ? min(L, L - C + row_last / G + 1) : 0;
+  const int n_super_w = kv_end_w > 0 ? (kv_end_w + 31) >> 5 : 0;
+
   int pos[NQ];
   size_t orow[NQ];
   u32x4 qop[NQ][KC];
@@ -88,12 +167,39 @@ prefill_mfma_kernel(PrefillArgs a) {
       qop[qt][kk] = valid ? *reinterpret_cast<const u32x4 *>(qp + (kk * 4 + grp) * 16)
                           : u32x4{0u, 0u, 0u, 0u};
   }
+  // the queries are in registers before the ring's loads are counted
+  wait_vm<0>();
 
-  const char *kc = static_cast<const char *>(a.k_cache);
-  const char *vc = static_cast<const char *>(a.v_cache);
-  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
-  const uint32_t koff = (uint32_t)(col * D * E + grp * 16);
-  const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);
+  // block-table entries are wave-uniform: read through the scalar cache
+  const __attribute__((address_space(4))) int32_t *trow =
+      (const __attribute__((address_space(4))) int32_t *)(a.block_tables +
+                                                          (size_t)s * a.max_blocks);
+  const size_t block_bytes = (size_t)Hkv * BS * D * 2;
+  const char *src_base = static_cast<const char *>(w < 2 ? a.k_cache : a.v_cache) +
+                         (size_t)g * BS * D * 2;
+  // this lane's source offset inside the piece, per 1 KiB block b
+  uint32_t lane_off[RG::LOADS];
+#pragma unroll
+  for (int b = 0; b < RG::LOADS; ++b) {
+    if (w < 2) {
+      const int rows_per_kib = 1024 / (2 * D);
+      const int r = b * rows_per_kib + lane / RG::CR, p = lane % RG::CR;
+      lane_off[b] = (uint32_t)(r * 2 * D + ((p ^ (r % RG::CR)) * 16));
+    } else {
+      lane_off[b] = (uint32_t)(b * 1024 + lane * 16);
+    }
+  }
+  // wavefront w fills piece w of super-tile n into stage n % S
+  auto issue = [&](int n) {
+    const int tb = 32 * n + 16 * (w & 1);
+    int phys = tb < L ? trow[tb / BS] : 0;  // a tile past the context: any block
+    phys = (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
+    const char *src = src_base + phys * block_bytes + (size_t)(tb % BS) * D * 2;
+    char *dst = ring + (n % S) * RG::TILE + w * RG::PIECE;
+#pragma unroll
+    for (int b = 0; b < RG::LOADS; ++b)
+      load_lds16(src + lane_off[b], dst + b * 1024);
+  };
 
   float m[NQ], l[NQ];
   f32x4 acc[NQ][NT];
@@ -104,46 +210,55 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[qt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const float c2 = a.scale_log2;  // > 0
 
-  // K/V tiles are read by every row block of the sequence: ordinary
-  // (cached) loads
-  auto load = [&](Tl &t, size_t tile_bytes) {
-    const char *kp = kc + tile_bytes + koff;
-    const char *vp = vc + tile_bytes + voff;
+  auto compute = [&](int n) {
+    const char *base = ring + (n % S) * RG::TILE;
+    u32x4 kop[2][KC], vop[2][NC];
 #pragma unroll
-    for (int c = 0; c < Tl::NC; ++c) t.k[c] = *reinterpret_cast<const u32x4 *>(kp + c * 64);
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-    for (int c = 0; c < Tl::NC; ++c) t.v[c] = *reinterpret_cast<const u32x4 *>(vp + c * 256);
-  };
-
-  auto compute = [&](Tl &t, int k) {
-    const int t0 = k * 16 + 4 * grp;  // this lane's first token of the tile
-    if (k * 16 + 16 > L) {
-      // tokens at or past L may hold anything (NaN included): zero their values
-      const int nvalid = max(0, min(4, L - t0));
-      const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-      const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+      for (int kk = 0; kk < KC; ++kk) {
+        const int c = kk * 4 + grp;
+        kop[st][kk] = lds16(base + st * RG::PIECE + col * 2 * D + ((c ^ (col % RG::CR)) * 16));
+      }
 #pragma unroll
-      for (int c = 0; c < Tl::NC; ++c) {
-        t.v[c][0] &= m01;
-        t.v[c][1] &= m23;
-        t.v[c][2] &= m01;
-        t.v[c][3] &= m23;
+      for (int u = 0; u < NC; ++u)
+        vop[st][u] = lds16(base + (2 + st) * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8);
+      const int t0 = 32 * n + 16 * st + 4 * grp;
+      if (32 * n + 16 * st + 16 > L) {
+        // tokens at or past L may hold anything (NaN included): zero them
+        const int nvalid = max(0, min(4, L - t0));
+        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          vop[st][u][0] &= m01;
+          vop[st][u][1] &= m23;
+          vop[st][u][2] &= m01;
+          vop[st][u][3] &= m23;
+        }
       }
     }
-    const bool masked = k >= k_full;
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      float x[2][4];
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[qt][kk], sacc);
-      float sc[4];
+      for (int st = 0; st < 2; ++st) {
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = sacc[i] * a.scale_log2;
-        if (masked && t0 + i > pos[qt]) sc[i] = -INFINITY;
+        for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(kop[st][kk], qop[qt][kk], sacc);
+        const int t0 = 32 * n + 16 * st + 4 * grp;
+        const bool masked = 32 * n + 16 * st + 15 > pos_first;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[st][i] = (masked && t0 + i > pos[qt]) ? -INFINITY : sacc[i];
       }
-      const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      // running maximum (base-2 units), moved only when a logit exceeds it
+      // by more than the slack somewhere in the wave
+      const float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                             fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      const float mb = xm * c2;
       if (wave_any(mb > m[qt] + kRescaleSlack)) {
         float mh = fmaxf(mb, __shfl_xor(mb, 16));
         mh = fmaxf(mh, __shfl_xor(mh, 32));
@@ -154,31 +269,56 @@ prefill_mfma_kernel(PrefillArgs a) {
         for (int nt = 0; nt < NT; ++nt) acc[qt][nt] *= alpha;
         m[qt] = m_new;
       }
-      const float m_use = m[qt] == -INFINITY ? 0.f : m[qt];
-      float r0, r1, r2, r3;
-      const uint32_t p01 = Ops::round2(fast_exp2(sc[0] - m_use), fast_exp2(sc[1] - m_use), r0, r1);
-      const uint32_t p23 = Ops::round2(fast_exp2(sc[2] - m_use), fast_exp2(sc[3] - m_use), r2, r3);
-      l[qt] += (r0 + r1) + (r2 + r3);
-      const u32x2 pb = {p01, p23};
-      // chunk u, words 2j..2j+1: the four tokens of dim 32u + 2*col + j
+      const float nm = m[qt] == -INFINITY ? 0.f : -m[qt];
+      float p[2][4];
 #pragma unroll
-      for (int u = 0; u < Tl::NC; ++u) {
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[st][i] = fast_exp2(__builtin_fmaf(x[st][i], c2, nm));
+      l[qt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      const u32x4 pb = {Ops::pack2(p[0][0], p[0][1]), Ops::pack2(p[0][2], p[0][3]),
+                        Ops::pack2(p[1][0], p[1][1]), Ops::pack2(p[1][2], p[1][3])};
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
-          acc[qt][2 * u + j] = Ops::pv(va, pb, acc[qt][2 * u + j]);
+          const u32x4 va = {vop[0][u][2 * j], vop[0][u][2 * j + 1], vop[1][u][2 * j],
+                            vop[1][u][2 * j + 1]};
+          acc[qt][2 * u + j] = Ops::pv32(va, pb, acc[qt][2 * u + j]);
         }
       }
     }
   };
 
-  if (n_tiles > 0)
-    walk_tiles<Tl, 1>(trow, 0, n_tiles, BS / 16, (unsigned)a.num_blocks, (size_t)g * BS * D * E,
-                      (size_t)Hkv * BS * D * E, (size_t)16 * D * E, load, compute);
+  // Pipeline: S - 1 super-tiles in flight.  Iteration n waits for its own
+  // loads of super-tile n (the loads of later super-tiles may stay
+  // outstanding), meets the other wavefronts at the barrier (then super-tile
+  // n is complete in LDS and everyone is done with super-tile n - 1), refills
+  // the stage super-tile n - 1 used, and computes on super-tile n.  Every
+  // super-tile costs each wavefront exactly RG::LOADS loads, so the counts
+  // below are exact.
+  const int n_pre = min(S - 1, n_super);
+  for (int n = 0; n < n_pre; ++n) issue(n);
+  for (int n = 0; n < n_super; ++n) {
+    const int later = min(S - 2, n_super - 1 - n);  // super-tiles issued after n
+    static_assert((S - 2) * RG::LOADS < 16, "vmcnt range");
+    if (later >= 2)
+      wait_vm<2 * RG::LOADS>();
+    else if (later == 1)
+      wait_vm<RG::LOADS>();
+    else
+      wait_vm<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (n + S - 1 < n_super) issue(n + S - 1);
+    if (n < n_super_w) compute(n);  // wave-uniform
+  }
 
   // normalise and store: n-tile 2u+j, row m = 4*grp + i is dim 32u + 2m + j
-  // of the lane's query row, so the two n-tiles of a chunk give two
-  // adjacent dims, stored as one 32-bit word
+  // of the lane's query row; the two n-tiles of a chunk give two adjacent
+  // dims, stored as one 32-bit word
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     float lt = l[qt] + __shfl_xor(l[qt], 16);
@@ -187,7 +327,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow[qt]);
 #pragma unroll
-    for (int u = 0; u < Tl::NC; ++u) {
+    for (int u = 0; u < NC; ++u) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * u + 2 * (4 * grp + i);
@@ -200,8 +340,9 @@ prefill_mfma_kernel(PrefillArgs a) {
 
 template <int QT, int D, int BS>
 static hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
-  const dim3 grid(a.num_kv_heads, a.num_seqs, a.q_blocks);
-  hipLaunchKernelGGL((prefill_mfma_kernel<QT, D, BS>), grid, dim3(kPrefillThreads), 0, st, a);
+  const int64_t n = prefill_grid(a.num_seqs, a.num_kv_heads, a.q_blocks);
+  hipLaunchKernelGGL((prefill_mfma_kernel<QT, D, BS>), dim3((unsigned)n), dim3(kPrefillThreads),
+                     0, st, a);
   return hipGetLastError();
 }
 
