@@ -60,7 +60,27 @@ hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
 // offset slot % BS.  One thread moves one 16-byte chunk of one (token,
 // KV head) key row - a single 16-byte store into the K tile - and the same
 // dims of the value row, which the token-grouped V layout spreads with a
-// stride of four elements.  Negative or out-of-pool slots write nothing.
+// stride of four elements: when four consecutive tokens of the batch fill a
+// whole group of four slots (a prompt or a chunk written in order), the
+// first of them writes the group's values as 16-byte units, otherwise every
+// token writes its own elements.  Negative or out-of-pool slots write
+// nothing.
+// Group of four consecutive slots of one block that token i's slot falls
+// in, if the four tokens b .. b+3 of the batch (b = i - slot % 4) fill
+// exactly those slots in order: then one thread (token b's) writes the
+// whole group's values as 16-byte units.  Returns b, or -1 when token i's
+// group is only partly written by this batch.  The slots are distinct (a
+// precondition), so a full group has exactly one such leader.
+__device__ __forceinline__ int64_t full_group_leader(const int64_t *slots, int64_t i,
+                                                     int64_t num_tokens, int64_t slot) {
+  const int64_t b = i - (slot & 3);
+  if (b < 0 || b + 3 >= num_tokens) return -1;
+  const int64_t s0 = slot - (slot & 3);
+  for (int j = 0; j < 4; ++j)
+    if (slots[b + j] != s0 + j) return -1;
+  return b;
+}
+
 template <int DT, int D, int BS>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(CacheWriteArgs a) {
   constexpr int E = Elem<DT>::bytes;
@@ -83,8 +103,41 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(CacheWriteArgs a
   const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k) + src * E);
   *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache) + (tile + (size_t)o * D + chunk * EPC) * E) = kx;
 
+  // values: the token-grouped layout keeps four consecutive slots of one
+  // dim together, elements (o/4)*4*D + d*4 + o%4 of the tile
+  const size_t vg = tile + (size_t)(o / 4) * 4 * D;  // the slot group
+  const int64_t lead = full_group_leader(a.slot_mapping, i, a.num_tokens, slot);
+  if (lead == i) {
+    // four tokens' EPC dims: EPC x 4 elements, contiguous, as 16-byte stores
+    const size_t vrow = (size_t)a.num_kv_heads * D;  // elements between tokens
+    u32x4 vt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      vt[t] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) +
+                                               (src + t * vrow) * E);
+    char *dst = static_cast<char *>(a.v_cache) + (vg + (size_t)chunk * EPC * 4) * E;
+    if constexpr (E == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        reinterpret_cast<u32x4 *>(dst)[e] = u32x4{vt[0][e], vt[1][e], vt[2][e], vt[3][e]};
+    } else {
+      // 16 bytes = two dims x four tokens; word w of dim pair q
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo[4] = {vt[0][q] & 0xffffu, vt[1][q] & 0xffffu, vt[2][q] & 0xffffu,
+                                vt[3][q] & 0xffffu};
+        const uint32_t hi[4] = {vt[0][q] >> 16, vt[1][q] >> 16, vt[2][q] >> 16, vt[3][q] >> 16};
+        reinterpret_cast<u32x4 *>(dst)[q] =
+            u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), hi[0] | (hi[1] << 16),
+                  hi[2] | (hi[3] << 16)};
+      }
+    }
+    return;
+  }
+  if (lead >= 0) return;  // the group's leader writes this token's values
+
   const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) + src * E);
-  const size_t vb = tile + (size_t)(o / 4) * 4 * D + (o % 4);
+  const size_t vb = vg + (o % 4);
   if constexpr (E == 4) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -116,7 +169,9 @@ static hipError_t launch_rac_d(const CacheWriteArgs &a, int block_size, hipStrea
 // lower-precision cache formats reduce the bytes per element).  Every
 // element x is stored as e4m3(x / scale), the quotient computed in IEEE
 // single precision.  One thread converts eight consecutive dims of one
-// (token, KV head) row: one 8-byte K store, eight V bytes four apart.
+// (token, KV head) row: one 8-byte K store, and eight V bytes four apart -
+// or, for the first token of four that fill a whole slot group, the
+// group's 32 value bytes of those dims as two 16-byte stores.
 template <int IT, int D, int BS>
 __global__ void __launch_bounds__(256) reshape_and_cache_fp8_kernel(CacheWriteArgs a) {
   constexpr int EI = Elem<IT>::bytes;
@@ -147,16 +202,44 @@ __global__ void __launch_bounds__(256) reshape_and_cache_fp8_kernel(CacheWriteAr
     }
   }
   uint32_t kq[2] = {0u, 0u};
-  uint8_t *vc = static_cast<uint8_t *>(a.v_cache);
-  const size_t vb = tile + (size_t)(o / 4) * 4 * D + (o % 4);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 8; ++e)
     kq[e / 4] |= e4m3_from_f32(elem<IT>(kw, e) / a.k_scale) << (8 * (e % 4));
-    vc[vb + (size_t)(chunk * 8 + e) * 4] =
-        static_cast<uint8_t>(e4m3_from_f32(elem<IT>(vw, e) / a.v_scale));
-  }
   *reinterpret_cast<u32x2 *>(static_cast<char *>(a.k_cache) + tile + (size_t)o * D + chunk * 8) =
       u32x2{kq[0], kq[1]};
+
+  uint8_t *vc = static_cast<uint8_t *>(a.v_cache);
+  const size_t vg = tile + (size_t)(o / 4) * 4 * D;
+  const int64_t lead = full_group_leader(a.slot_mapping, i, a.num_tokens, slot);
+  if (lead == i) {
+    // the group's four tokens, eight dims: one word (four tokens) per dim
+    uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    const size_t vrow = (size_t)a.num_kv_heads * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t tw[8 * EI / 4];
+#pragma unroll
+      for (int u = 0; u < 8 * EI / 16; ++u) {
+        const u32x4 y = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) +
+                                                         (src + t * vrow) * EI + 16 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tw[4 * u + e] = y[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        word[e] |= e4m3_from_f32(elem<IT>(tw, e) / a.v_scale) << (8 * t);
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(vc + vg + (size_t)chunk * 8 * 4);
+    dst[0] = u32x4{word[0], word[1], word[2], word[3]};
+    dst[1] = u32x4{word[4], word[5], word[6], word[7]};
+    return;
+  }
+  if (lead >= 0) return;  // the group's leader writes this token's values
+  const size_t vb = vg + (o % 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    vc[vb + (size_t)(chunk * 8 + e) * 4] =
+        static_cast<uint8_t>(e4m3_from_f32(elem<IT>(vw, e) / a.v_scale));
 }
 
 template <int DT, int CT>
