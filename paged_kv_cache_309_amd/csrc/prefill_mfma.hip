@@ -15,7 +15,8 @@
 // Work: the query rows of one (sequence, KV head) are the chunk's tokens
 // times the G query heads of the group, row r = token (r / G), head (r % G).
 // A workgroup (4 wavefronts) takes 128 consecutive rows, each wavefront 32
-// of them (two row tiles of 16).  The workgroup walks the K/V of the
+// of them (two row tiles of 16; with 64 rows per wavefront the registers
+// allow one wavefront per SIMD only, which measured slower).  The workgroup walks the K/V of the
 // sequence in 32-token super-tiles through the block table: the four
 // wavefronts copy a super-tile (two 16-token tiles of K and of V) from HBM
 // into a ring of LDS stages with direct global-to-LDS loads, three
@@ -44,8 +45,11 @@
 // XCD's L2 while its row blocks run.
 //
 // Probabilities enter the value product rounded to the 16-bit type of q
-// (nearest even, one packed conversion per pair); the running sums add the
-// fp32 values; accumulation is fp32.
+// (nearest even, one packed conversion per pair).  The running sum of each
+// row comes out of one more 16x16x32 product with an A operand of ones, so
+// it adds exactly the rounded weights the value product applied, and the
+// softmax stays off the vector ALUs as far as possible: per logit one fused
+// multiply-add and one exp2, plus the running maximum.  Accumulation is fp32.
 #include "mfma_ops.h"
 
 namespace pkv {
@@ -201,19 +205,22 @@ prefill_mfma_kernel(PrefillArgs a) {
       load_lds16(src + lane_off[b], dst + b * 1024);
   };
 
-  float m[NQ], l[NQ];
-  f32x4 acc[NQ][NT];
+  float m[NQ];
+  f32x4 acc[NQ][NT], lsum[NQ];
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     m[qt] = -INFINITY;
-    l[qt] = 0.f;
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[qt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;  // > 0
+  const uint32_t one2 = Ops::pack2(1.f, 1.f);
+  const u32x4 ones = {one2, one2, one2, one2};
 
   auto compute = [&](int n) {
     const char *base = ring + (n % S) * RG::TILE;
+    const bool diag = 32 * n + 31 > pos_first;
     u32x4 kop[2][KC], vop[2][NC];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -248,11 +255,17 @@ prefill_mfma_kernel(PrefillArgs a) {
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(kop[st][kk], qop[qt][kk], sacc);
-        const int t0 = 32 * n + 16 * st + 4 * grp;
-        const bool masked = 32 * n + 16 * st + 15 > pos_first;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          x[st][i] = (masked && t0 + i > pos[qt]) ? -INFINITY : sacc[i];
+        for (int i = 0; i < 4; ++i) x[st][i] = sacc[i];
+      }
+      if (diag) {  // wave-uniform: only tiles that reach past the first row
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int t0 = 32 * n + 16 * st + 4 * grp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + i > pos[qt]) x[st][i] = -INFINITY;
+        }
       }
       // running maximum (base-2 units), moved only when a logit exceeds it
       // by more than the slack somewhere in the wave
@@ -264,7 +277,7 @@ prefill_mfma_kernel(PrefillArgs a) {
         mh = fmaxf(mh, __shfl_xor(mh, 32));
         const float m_new = fmaxf(m[qt], mh);
         const float alpha = fast_exp2(m[qt] - (m_new == -INFINITY ? 0.f : m_new));
-        l[qt] *= alpha;
+        lsum[qt] *= alpha;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[qt][nt] *= alpha;
         m[qt] = m_new;
@@ -275,8 +288,6 @@ prefill_mfma_kernel(PrefillArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[st][i] = fast_exp2(__builtin_fmaf(x[st][i], c2, nm));
-      l[qt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
       const u32x4 pb = {Ops::pack2(p[0][0], p[0][1]), Ops::pack2(p[0][2], p[0][3]),
                         Ops::pack2(p[1][0], p[1][1]), Ops::pack2(p[1][2], p[1][3])};
 #pragma unroll
@@ -288,6 +299,7 @@ prefill_mfma_kernel(PrefillArgs a) {
           acc[qt][2 * u + j] = Ops::pv32(va, pb, acc[qt][2 * u + j]);
         }
       }
+      lsum[qt] = Ops::pv32(ones, pb, lsum[qt]);  // every row: the sum of the weights
     }
   };
 
@@ -321,8 +333,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   // dims, stored as one 32-bit word
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
-    float lt = l[qt] + __shfl_xor(l[qt], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lsum[qt][0];
     if (row0 + qt * 16 + col > row_last) continue;  // no row in this column
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow[qt]);
