@@ -216,7 +216,12 @@ decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  if (n_mine > 0)
+  // 8-bit tiles are half the bytes: keep two of them in flight per wave
+  if (n_mine > 0 && F8)
+    walk_tiles3<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+                    (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
+                    load, compute);
+  else if (n_mine > 0)
     walk_tiles<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
                    (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
                    load, compute);

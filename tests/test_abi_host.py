@@ -175,3 +175,28 @@ def test_swap_blocks_rejects_bad_arguments():
     assert sw(d, dv=C + 4096) == ERR["PKV_ERR_ALIAS"]
     assert sw(d, mp=C + 64) == ERR["PKV_ERR_ALIAS"]
     assert sw(d, n=0, sk=None, sv=None, dk=None, dv=None, mp=None) == 0
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = _lib.lib()
+
+    def pf(d, bs=16, T=32, mq=16, out=A, q=B, kc=C, vc=DQ, bt=E, cl=F, qsl=W):
+        return lib.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, 0.1, bs,
+                                           T, mq, ctypes.byref(d), None)
+    d = dims()
+    assert pf(d, bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
+    assert pf(dims(D=96)) == ERR["PKV_ERR_HEAD_DIM"]
+    assert pf(dims(dt=0)) == ERR["PKV_ERR_DTYPE"]          # fp32: no prefill
+    assert pf(dims(dt=3)) == ERR["PKV_ERR_DTYPE"]
+    assert pf(dims(Hq=6, Hkv=4)) == ERR["PKV_ERR_HEADS"]
+    assert pf(d, T=-1) == ERR["PKV_ERR_SHAPE"]
+    assert pf(d, mq=-1) == ERR["PKV_ERR_SHAPE"]
+    assert pf(d, qsl=None) == ERR["PKV_ERR_NULL"]
+    assert pf(d, out=None) == ERR["PKV_ERR_NULL"]
+    assert pf(d, q=B + 8) == ERR["PKV_ERR_ALIGN"]
+    assert pf(d, qsl=W + 2) == ERR["PKV_ERR_ALIGN"]
+    # out [32, 8, 128] bf16 = 64 KiB: q 4 KiB after it overlaps
+    assert pf(d, q=A + 4096) == ERR["PKV_ERR_ALIAS"]
+    assert pf(d, qsl=A + 64) == ERR["PKV_ERR_ALIAS"]
+    assert pf(d, T=0, out=None, q=None) == 0
+    assert pf(dims(S_=0), out=None) == 0
