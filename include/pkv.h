@@ -218,11 +218,12 @@ int paged_attention_decode_split(void *out, const void *q, const void *k_cache,
  *                     start[num_seqs] = num_query_tokens (device)
  *   max_query_len     an upper bound of every C_s (host-side; sizes the grid)
  *   k_cache, v_cache, block_tables, context_lens: as for decode.
- * dims->dtype must be PKV_F16 or PKV_BF16 (the matrix-core kernel; fp32
- * returns PKV_ERR_DTYPE).  Probabilities enter the value product rounded to
- * dims->dtype, accumulation is fp32.  Preconditions (device data, not
- * checked): C_s <= max_query_len and C_s <= context_lens[s]; rows of a
- * query token whose position would be negative are written as zeros.
+ * fp16 and bf16 run on the matrix cores: probabilities enter the value
+ * product rounded to dims->dtype, accumulation is fp32.  fp32 runs on the
+ * vector ALUs (one workgroup per query token and head, fp32 throughout;
+ * num_query_tokens * num_heads must fit in an int).  Preconditions (device
+ * data, not checked): C_s <= max_query_len and C_s <= context_lens[s]; rows
+ * of a query token whose position would be negative are written as zeros.
  * Asynchronous on `stream`; returns a pkv_status.
  */
 int paged_attention_prefill(void *out, const void *q, const void *k_cache,
@@ -263,6 +264,16 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
                                const int32_t *context_lens, float scale,
                                int block_size, float k_scale, float v_scale,
                                const pkv_dims *dims, pkv_stream_t stream);
+
+/* Chunked prefill over 8-bit caches (same rows and causality as
+ * paged_attention_prefill), on the vector kernel for every dims->dtype. */
+int paged_attention_prefill_fp8(void *out, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                const int32_t *context_lens,
+                                const int32_t *query_start_loc, float scale,
+                                int block_size, int num_query_tokens,
+                                int max_query_len, float k_scale, float v_scale,
+                                const pkv_dims *dims, pkv_stream_t stream);
 
 int paged_attention_decode_split_fp8(void *out, const void *q,
                                      const void *k_cache, const void *v_cache,

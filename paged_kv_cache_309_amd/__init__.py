@@ -173,7 +173,8 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor,
                             query_start_loc: torch.Tensor, scale: float,
                             max_query_len: int | None = None,
                             block_size: int | None = None,
-                            stream=None) -> torch.Tensor:
+                            stream=None, k_scale: float = 1.0,
+                            v_scale: float = 1.0) -> torch.Tensor:
     """Chunked prefill: q / out [T, Hq, D] hold the chunk tokens of every
     sequence (rows query_start_loc[s] .. query_start_loc[s+1]-1, the last
     tokens of its context, whose K/V are already in the cache); each
@@ -185,6 +186,13 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor,
     dims = PkvDims(S, q.shape[1], Hkv, q.shape[2], NB, block_tables.shape[1],
                    _dtype(q))
     mq = T if max_query_len is None else int(max_query_len)
+    if _is_fp8(k_cache):
+        _lib.check(_lib.lib().paged_attention_prefill_fp8(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+            float(scale), bs, T, mq, float(k_scale), float(v_scale),
+            ctypes.byref(dims), _stream(stream)))
+        return out
     _lib.check(_lib.lib().paged_attention_prefill(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start_loc), float(scale), bs, T, mq,

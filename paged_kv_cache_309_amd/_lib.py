@@ -35,7 +35,7 @@ EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "swap_blocks", "pkv_bm_create_with_host", "pkv_bm_swap_out",
            "pkv_bm_swap_in", "pkv_bm_num_free_host_blocks",
            "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table",
-           "paged_attention_prefill")
+           "paged_attention_prefill", "paged_attention_prefill_fp8")
 
 
 class PkvDims(ctypes.Structure):
@@ -106,6 +106,11 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_prefill.restype = I
     lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P,
                                             ctypes.c_float, I, I, I, D, P]
+    lib.paged_attention_prefill_fp8.restype = I
+    lib.paged_attention_prefill_fp8.argtypes = [P, P, P, P, P, P, P,
+                                                ctypes.c_float, I, I, I,
+                                                ctypes.c_float, ctypes.c_float,
+                                                D, P]
     lib.swap_blocks.restype = I
     lib.swap_blocks.argtypes = [P, P, P, P, P, I, I32, I32, I, D, P]
     lib.pkv_bm_create_with_host.restype = I

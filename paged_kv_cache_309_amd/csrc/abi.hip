@@ -235,9 +235,11 @@ int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
   int rc = check_decode(dims, block_size, &sb, &cb, cache_dtype == kCacheSame ? 0 : 1);
   if (rc != PKV_OK) return rc;
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
-  // the matrix-core kernel takes 16-bit queries and caches
-  if (dims->dtype == PKV_F32 || cache_dtype != kCacheSame) return PKV_ERR_DTYPE;
   if (num_query_tokens < 0 || max_query_len < 0) return PKV_ERR_SHAPE;
+  // fp16/bf16 queries over 16-bit caches run on the matrix cores; fp32 and
+  // 8-bit caches on the vector kernel, one workgroup per (query row, head)
+  const bool on_mfma = dims->dtype != PKV_F32 && cache_dtype == kCacheSame;
+  if (!on_mfma && (int64_t)num_query_tokens * dims->num_heads > INT_MAX) return PKV_ERR_SHAPE;
   const int G = dims->num_heads / dims->num_kv_heads;
   const u128 qb = (u128)num_query_tokens * (u128)dims->num_heads * (u128)dims->head_dim *
                   (u128)elem_bytes(dims->dtype);
@@ -263,6 +265,17 @@ int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
       overlap(out, ob, block_tables, tb) || overlap(out, ob, context_lens, lb) ||
       overlap(out, ob, query_start_loc, lb + 4))
     return PKV_ERR_ALIAS;
+  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!on_mfma) {
+    pkv::DecodeArgs d = make_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  block_size, dims, k_scale, v_scale);
+    d.query_start_loc = query_start_loc;
+    d.num_query_tokens = num_query_tokens;
+    const hipError_t err =
+        pkv::launch_prefill_vector(d, dims->dtype, ct, dims->head_dim, block_size, st);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  }
   pkv::PrefillArgs a{};
   a.out = out;
   a.q = q;
@@ -280,10 +293,8 @@ int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
   a.max_blocks = dims->num_blocks > 0 ? dims->max_blocks_per_seq : 0;
   a.num_query_tokens = num_query_tokens;
   a.q_blocks = (int)q_blocks;
-  const int ct = cache_dtype == kCacheSame ? dims->dtype : cache_dtype;
   const hipError_t err =
-      pkv::launch_prefill_mfma(a, dims->dtype, ct, dims->head_dim, block_size, max_query_len,
-                               reinterpret_cast<hipStream_t>(stream));
+      pkv::launch_prefill_mfma(a, dims->dtype, ct, dims->head_dim, block_size, max_query_len, st);
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -378,6 +389,17 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache,
   return prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
                  block_size, num_query_tokens, max_query_len, dims, stream, kCacheSame, 1.f,
                  1.f);
+}
+
+int paged_attention_prefill_fp8(void *out, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                const int32_t *context_lens, const int32_t *query_start_loc,
+                                float scale, int block_size, int num_query_tokens,
+                                int max_query_len, float k_scale, float v_scale,
+                                const pkv_dims *dims, pkv_stream_t stream) {
+  return prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                 block_size, num_query_tokens, max_query_len, dims, stream, pkv::DT_FP8, k_scale,
+                 v_scale);
 }
 
 int paged_attention_split_workspace_bytes(const pkv_dims *dims, int block_size,

@@ -14,6 +14,11 @@
 //
 // Used for multi-head attention (one KV head per query head), and for fp32
 // or very wide query groups, where every query head re-reads its KV head.
+// With MQ the same kernel serves chunked prefill where the matrix-core
+// kernel does not (fp32, 8-bit caches): a workgroup then takes one (query
+// token, query head) and attends to the token's causal prefix ("Inside
+// vLLM: How PagedAttention Eliminates KV-Cache Memory Waste", section
+// "Continuous Batching and Chunked Prefill").
 //
 // Work decomposition (gfx950, wave64):
 //  * a workgroup is 4 wavefronts; the sequence's context is cut into
@@ -49,8 +54,20 @@ struct VecTile {
   uint32_t v[VW];
 };
 
+// Sequence of query row r: the s with query_start_loc[s] <= r <
+// query_start_loc[s+1] (binary search over the nondecreasing starts).
+__device__ __forceinline__ int seq_of_row(const int32_t *qsl, int num_seqs, int r) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // QT: element type of q and out; CT: of the caches (QT, or 8-bit E4M3)
-template <int QT, int CT, int D, int BS, bool SPLIT>
+template <int QT, int CT, int D, int BS, bool SPLIT, bool MQ = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_vector_kernel(DecodeArgs a) {
   using Tl = VecTile<CT, D>;
@@ -58,8 +75,11 @@ decode_vector_kernel(DecodeArgs a) {
   constexpr int KWQ = Tl::DQ * Elem<QT>::bytes / 4;  // words of q per lane
   constexpr int NACC = Tl::VI * Tl::DPV;  // == D / 16
 
-  const int h = blockIdx.x, part = blockIdx.z;
+  static_assert(!(MQ && SPLIT), "multi-query runs single-pass");
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+  // multi-query: one workgroup per (query row, head), flattened on x
+  const int h = MQ ? (int)(blockIdx.x % Hq) : (int)blockIdx.x, part = blockIdx.z;
+  const int qrow = MQ ? (int)(blockIdx.x / Hq) : 0;
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
 
@@ -68,18 +88,26 @@ decode_vector_kernel(DecodeArgs a) {
   __shared__ float sm_acc[16][D];
   __shared__ float sm_m[16], sm_l[16];
   static_assert(sizeof(sm_acc) >= kOrderMaxSeqs * sizeof(int), "order scratch");
-  const int s = SPLIT ? (int)blockIdx.y
-                      : longest_first_seq<kDecodeThreads>(
-                            a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,
-                            reinterpret_cast<int *>(&sm_acc[0][0]));
+  const int s = MQ ? seq_of_row(a.query_start_loc, a.num_seqs, qrow)
+               : SPLIT ? (int)blockIdx.y
+                       : longest_first_seq<kDecodeThreads>(
+                             a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,
+                             reinterpret_cast<int *>(&sm_acc[0][0]));
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, r = lane >> 4, c = lane & 15;
 
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks * BS));
+  if constexpr (MQ) {
+    // the chunk is the last C tokens of the context; row qrow attends to
+    // the tokens up to and including its own position
+    const int q0 = a.query_start_loc[s];
+    const int C = a.query_start_loc[s + 1] - q0;
+    L = max(0, min(L, L - C + (qrow - q0) + 1));
+  }
   const int tok_begin = SPLIT ? part * a.part_tokens : 0;
   const int tok_end = SPLIT ? min(L, tok_begin + a.part_tokens) : L;
-  const size_t orow = ((size_t)s * Hq + h) * D;
+  const size_t orow = ((size_t)(MQ ? qrow : s) * Hq + h) * D;
 
   if (tok_begin >= tok_end) {
     if (!SPLIT) {
@@ -276,6 +304,41 @@ static hipError_t launch_vec(const DecodeArgs &a, bool split, hipStream_t st) {
     hipLaunchKernelGGL((decode_vector_kernel<QT, CT, D, BS, false>), grid,
                        dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int QT, int CT, int D, int BS>
+static hipError_t launch_vec_mq(const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.num_query_tokens * a.num_heads));
+  hipLaunchKernelGGL((decode_vector_kernel<QT, CT, D, BS, false, true>), grid,
+                     dim3(kDecodeThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int QT, int CT>
+static hipError_t launch_vec_mq_dt(const DecodeArgs &a, int head_dim, int block_size,
+                                   hipStream_t st) {
+  if (head_dim == 128)
+    return block_size == 16 ? launch_vec_mq<QT, CT, 128, 16>(a, st)
+                            : launch_vec_mq<QT, CT, 128, 32>(a, st);
+  return block_size == 16 ? launch_vec_mq<QT, CT, 64, 16>(a, st)
+                          : launch_vec_mq<QT, CT, 64, 32>(a, st);
+}
+
+hipError_t launch_prefill_vector(const DecodeArgs &a, int dtype, int cache_dtype, int head_dim,
+                                 int block_size, hipStream_t st) {
+  if (a.num_query_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  if (cache_dtype == DT_FP8) {
+    switch (dtype) {
+      case DT_F32: return launch_vec_mq_dt<DT_F32, DT_FP8>(a, head_dim, block_size, st);
+      case DT_F16: return launch_vec_mq_dt<DT_F16, DT_FP8>(a, head_dim, block_size, st);
+      default: return launch_vec_mq_dt<DT_BF16, DT_FP8>(a, head_dim, block_size, st);
+    }
+  }
+  switch (dtype) {
+    case DT_F32: return launch_vec_mq_dt<DT_F32, DT_F32>(a, head_dim, block_size, st);
+    case DT_F16: return launch_vec_mq_dt<DT_F16, DT_F16>(a, head_dim, block_size, st);
+    default: return launch_vec_mq_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, st);
+  }
 }
 
 template <int QT, int CT>

@@ -34,6 +34,12 @@ struct DecodeArgs {
   int block_size;
   int part_tokens;        // tokens per partition (split); unused otherwise
   int num_parts;          // partitions per sequence (1 for single pass)
+  // multi-query (chunked prefill) on the vector kernel: q / out hold
+  // num_query_tokens rows; sequence s's rows are query_start_loc[s] ..
+  // query_start_loc[s+1]-1, the last tokens of its context (causal).
+  // nullptr for decode.
+  const int32_t *query_start_loc;
+  int num_query_tokens;
 };
 
 struct CacheWriteArgs {
@@ -97,6 +103,10 @@ hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
 hipError_t launch_reshape_and_cache(const CacheWriteArgs &a, int dtype,
                                     int cache_dtype, int head_dim,
                                     int block_size, hipStream_t st);
+// Multi-query attention on the vector kernel, one workgroup per (query
+// row, query head): the prefill path for fp32 and for 8-bit caches.
+hipError_t launch_prefill_vector(const DecodeArgs &a, int dtype, int cache_dtype,
+                                 int head_dim, int block_size, hipStream_t st);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
                                int head_dim, int block_size, int max_query_len,
                                hipStream_t st);

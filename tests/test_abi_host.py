@@ -186,7 +186,6 @@ def test_prefill_rejects_bad_arguments():
     d = dims()
     assert pf(d, bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
     assert pf(dims(D=96)) == ERR["PKV_ERR_HEAD_DIM"]
-    assert pf(dims(dt=0)) == ERR["PKV_ERR_DTYPE"]          # fp32: no prefill
     assert pf(dims(dt=3)) == ERR["PKV_ERR_DTYPE"]
     assert pf(dims(Hq=6, Hkv=4)) == ERR["PKV_ERR_HEADS"]
     assert pf(d, T=-1) == ERR["PKV_ERR_SHAPE"]
