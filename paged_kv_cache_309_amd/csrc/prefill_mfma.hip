@@ -247,47 +247,65 @@ prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
+    // logits of both row tiles first, so that one tile's softmax can run on
+    // the vector ALUs while the other's products are still in the matrix
+    // cores
+    float x[NQ][2][4];
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-      float x[2][4];
+    for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(kop[st][kk], qop[qt][kk], sacc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[st][i] = sacc[i];
+        for (int i = 0; i < 4; ++i) x[qt][st][i] = sacc[i];
       }
-      if (diag) {  // wave-uniform: only tiles that reach past the first row
+    if (diag) {  // wave-uniform: only tiles that reach past the first row
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int t0 = 32 * n + 16 * st + 4 * grp;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t0 + i > pos[qt]) x[st][i] = -INFINITY;
+            if (t0 + i > pos[qt]) x[qt][st][i] = -INFINITY;
+        }
+    }
+    // running maxima (base-2 units), moved only when a logit exceeds one by
+    // more than the slack somewhere in the wave: one test for all row tiles
+    float mb[NQ];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      const float xm = fmaxf(fmaxf(fmaxf(x[qt][0][0], x[qt][0][1]), fmaxf(x[qt][0][2], x[qt][0][3])),
+                             fmaxf(fmaxf(x[qt][1][0], x[qt][1][1]), fmaxf(x[qt][1][2], x[qt][1][3])));
+      mb[qt] = xm * c2;
+      grow = grow || mb[qt] > m[qt] + kRescaleSlack;
+    }
+    if (wave_any(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) {
+        float mh = fmaxf(mb[qt], __shfl_xor(mb[qt], 16));
+        mh = fmaxf(mh, __shfl_xor(mh, 32));
+        if (wave_any(mh > m[qt] + kRescaleSlack)) {
+          const float m_new = fmaxf(m[qt], mh);
+          const float alpha = fast_exp2(m[qt] - (m_new == -INFINITY ? 0.f : m_new));
+          lsum[qt] *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[qt][nt] *= alpha;
+          m[qt] = m_new;
         }
       }
-      // running maximum (base-2 units), moved only when a logit exceeds it
-      // by more than the slack somewhere in the wave
-      const float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                             fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      const float mb = xm * c2;
-      if (wave_any(mb > m[qt] + kRescaleSlack)) {
-        float mh = fmaxf(mb, __shfl_xor(mb, 16));
-        mh = fmaxf(mh, __shfl_xor(mh, 32));
-        const float m_new = fmaxf(m[qt], mh);
-        const float alpha = fast_exp2(m[qt] - (m_new == -INFINITY ? 0.f : m_new));
-        lsum[qt] *= alpha;
+    }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[qt][nt] *= alpha;
-        m[qt] = m_new;
-      }
+    for (int qt = 0; qt < NQ; ++qt) {
       const float nm = m[qt] == -INFINITY ? 0.f : -m[qt];
       float p[2][4];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[st][i] = fast_exp2(__builtin_fmaf(x[st][i], c2, nm));
+        for (int i = 0; i < 4; ++i) p[st][i] = fast_exp2(__builtin_fmaf(x[qt][st][i], c2, nm));
       const u32x4 pb = {Ops::pack2(p[0][0], p[0][1]), Ops::pack2(p[0][2], p[0][3]),
                         Ops::pack2(p[1][0], p[1][1]), Ops::pack2(p[1][2], p[1][3])};
 #pragma unroll
