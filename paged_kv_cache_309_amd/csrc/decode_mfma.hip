@@ -31,7 +31,8 @@
 //
 // The probabilities enter the value product as a high and a low
 // half-precision part (p = hi + lo to about 16 significant bits), so the
-// weights keep near-fp32 precision.
+// weights keep near-fp32 precision.  Over 8-bit caches, whose values carry
+// 4 significant bits, one operand rounded to the 16-bit type is used.
 #include "mfma_ops.h"
 
 namespace pkv {
@@ -184,25 +185,29 @@ decode_mfma_kernel(DecodeArgs a) {
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-
-    uint32_t h01, l01, h23, l23;
-    Ops::split2(p[0], p[1], h01, l01);
-    Ops::split2(p[2], p[3], h23, l23);
-    const u32x2 phi = {h01, h23};
-    const u32x2 plo = {l01, l23};
     if constexpr (F8) {
+      // values with 4 significant bits: one probability operand rounded to
+      // the 16-bit type (8 or 11 bits) is ample, and the sum adds exactly
+      // the rounded weights
+      float r0, r1, r2, r3;
+      const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
+      l += (r0 + r1) + (r2 + r3);
       // chunk u, word j: the four tokens of dim 64u + 4*col + j -> n-tile 4u+j
 #pragma unroll
       for (int u = 0; u < Tl::NC; ++u) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const u32x2 va = {fp8x2_to_16<QT>(t.v[u][j], false), fp8x2_to_16<QT>(t.v[u][j], true)};
-          acc[4 * u + j] = Ops::pv(va, phi, acc[4 * u + j]);
-          acc[4 * u + j] = Ops::pv(va, plo, acc[4 * u + j]);
+          acc[4 * u + j] = Ops::pv(va, pr, acc[4 * u + j]);
         }
       }
     } else {
+      l += (p[0] + p[1]) + (p[2] + p[3]);
+      uint32_t h01, l01, h23, l23;
+      Ops::split2(p[0], p[1], h01, l01);
+      Ops::split2(p[2], p[3], h23, l23);
+      const u32x2 phi = {h01, h23};
+      const u32x2 plo = {l01, l23};
       // chunk u, words 2j..2j+1: the four tokens of dim 32u + 2*col + j
 #pragma unroll
       for (int u = 0; u < Tl::NC; ++u) {
