@@ -221,15 +221,18 @@ decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // 8-bit tiles are half the bytes: keep two of them in flight per wave
+  // tiles in flight per wave while one is computed: three of the 2 KiB
+  // tiles of 8-bit caches, two of the 4 KiB 16-bit tiles (measured: 8-bit
+  // gqa70b 165 -> 154 us from one to three, 16-bit 278 -> 271 us from one
+  // to two)
   if (n_mine > 0 && F8)
-    walk_tiles3<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
-                    (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
-                    load, compute);
+    walk_tiles_n<Tl, 4>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+                        (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
+                        load, compute);
   else if (n_mine > 0)
-    walk_tiles<Tl>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
-                   (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
-                   load, compute);
+    walk_tiles_n<Tl, 3>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+                        (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
+                        load, compute);
 
   // ---- merge the 4 wavefronts through LDS ----
   float lt = l + __shfl_xor(l, 16);

@@ -234,23 +234,24 @@ __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mi
   if (n < n_mine) compute(ta, n);
 }
 
-// The same walk with two tiles in flight while one is computed (three
-// buffers in rotation): for small tiles (8-bit caches), where one tile of
-// lookahead leaves too few bytes in flight per wavefront to cover the
-// memory latency.
-template <class Tile, int STRIDE = 4, class Load, class Compute>
-__device__ __forceinline__ void walk_tiles3(const int32_t *trow, int k0, int n_mine,
-                                            int subs, unsigned num_blocks,
-                                            size_t head_off_bytes,
-                                            size_t block_bytes, size_t sub_bytes,
-                                            Load load, Compute compute) {
+// The same walk with NBUF - 1 tiles in flight while one is computed
+// (NBUF buffers in rotation): for small tiles (8-bit caches), where one
+// tile of lookahead leaves too few bytes in flight per wavefront to cover
+// the memory latency.
+template <class Tile, int NBUF, int STRIDE = 4, class Load, class Compute>
+__device__ __forceinline__ void walk_tiles_n(const int32_t *trow, int k0, int n_mine,
+                                             int subs, unsigned num_blocks,
+                                             size_t head_off_bytes,
+                                             size_t block_bytes, size_t sub_bytes,
+                                             Load load, Compute compute) {
+  static_assert(NBUF >= 2, "at least two buffers");
   const int lane = threadIdx.x & 63;
   auto fetch = [&](int n0) -> int {
     const int n = n0 + lane;
     return n < n_mine ? trow[(k0 + STRIDE * n) / subs] : 0;
   };
-  // entries of tiles [64c, 64c + 64) live in ent[c % 2]; offset_of is
-  // called with increasing n, at most two tiles ahead of the computed one
+  // table entries of tiles [cur_base, cur_base + 64) are in ent_cur, the
+  // next 64 in ent_nxt; offset_of is called with n increasing by one
   int ent_cur = fetch(0);
   int ent_nxt = n_mine > 64 ? fetch(64) : 0;
   int cur_base = 0;
@@ -265,20 +266,22 @@ __device__ __forceinline__ void walk_tiles3(const int32_t *trow, int k0, int n_m
     const int k = k0 + STRIDE * n;
     return (size_t)phys * block_bytes + head_off_bytes + (size_t)(k % subs) * sub_bytes;
   };
-  Tile ta, tb, tc;
-  if (n_mine > 0) load(ta, offset_of(0));
-  if (n_mine > 1) load(tb, offset_of(1));
+  // invariant at the top of the loop: t[b] holds tile n + b, b < NBUF - 1
+  Tile t[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (b < n_mine) load(t[b], offset_of(b));
   int n = 0;
-  for (; n + 2 < n_mine; n += 3) {
-    load(tc, offset_of(n + 2));
-    compute(ta, n);
-    if (n + 3 < n_mine) load(ta, offset_of(n + 3));
-    compute(tb, n + 1);
-    if (n + 4 < n_mine) load(tb, offset_of(n + 4));
-    compute(tc, n + 2);
+  for (; n + NBUF - 1 < n_mine; n += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      if (n + b + NBUF - 1 < n_mine) load(t[(b + NBUF - 1) % NBUF], offset_of(n + b + NBUF - 1));
+      compute(t[b], n + b);
+    }
   }
-  if (n < n_mine) compute(ta, n);
-  if (n + 1 < n_mine) compute(tb, n + 1);
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (n + b < n_mine) compute(t[b], n + b);
 }
 
 }  // namespace pkv
