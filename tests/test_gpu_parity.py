@@ -240,3 +240,38 @@ def test_edge_contexts(dtype):
         # one token: the output is that token's value, exactly
         v0 = to_f64(to_torch(w.kv_v[w.token_rows[1][0]], dtype))
         assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,dtype", [(1024, 2, 2, "f16"), (1025, 2, 2, "bf16"),
+                                            (1500, 8, 2, "bf16"), (1300, 4, 4, "f32")])
+def test_many_sequences(S, Hq, Hkv, dtype):
+    """More sequences than the in-workgroup longest-first order handles
+    (1024): the grid order is kept, the result is the same."""
+    w = wl.random_case(9000 + S, num_seqs=S, max_len=60, num_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=64, block_size=16, dtype=dtype,
+                       pool_factor=1.3)
+    print_case("many", w)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    for variant in ("single", "split"):
+        got = to_f64(dev.decode(kd, vd, variant=variant, partition=32))
+        compare(got, want, dtype, f"S={S} {variant}")
+
+
+def test_table_wider_than_the_order_key():
+    """A block table of 2^17 entries (2^21 tokens at 16 per block): the
+    longest-first keys would overflow, so the grid order is kept."""
+    w = wl.random_case(9100, num_seqs=3, max_len=90, num_heads=4, num_kv_heads=2,
+                       head_dim=64, block_size=16, dtype="bf16", pool_factor=1.5)
+    MB = 1 << 17
+    tables = np.full((w.num_seqs, MB), -1, np.int32)
+    tables[:, :w.block_tables.shape[1]] = w.block_tables
+    w = wl.Workload(**{**w.__dict__, "block_tables": tables, "max_blocks_per_seq": MB})
+    print_case("wide table", w)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    compare(to_f64(dev.decode(kd, vd)), want, "bf16", "wide table")
