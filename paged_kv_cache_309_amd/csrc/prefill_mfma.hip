@@ -193,11 +193,16 @@ prefill_mfma_kernel(PrefillArgs a) {
       lane_off[b] = (uint32_t)(b * 1024 + lane * 16);
     }
   }
-  // wavefront w fills piece w of super-tile n into stage n % S
-  auto issue = [&](int n) {
+  // physical block of this wavefront's piece of super-tile n (a tile past
+  // the context: any block, its contents are masked)
+  auto lookup = [&](int n) -> int {
     const int tb = 32 * n + 16 * (w & 1);
-    int phys = tb < L ? trow[tb / BS] : 0;  // a tile past the context: any block
-    phys = (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
+    const int phys = tb < L ? trow[tb / BS] : 0;
+    return (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
+  };
+  // wavefront w fills piece w of super-tile n into stage n % S
+  auto issue = [&](int n, int phys) {
+    const int tb = 32 * n + 16 * (w & 1);
     const char *src = src_base + phys * block_bytes + (size_t)(tb % BS) * D * 2;
     char *dst = ring + (n % S) * RG::TILE + w * RG::PIECE;
 #pragma unroll
@@ -329,7 +334,10 @@ prefill_mfma_kernel(PrefillArgs a) {
   // super-tile costs each wavefront exactly RG::LOADS loads, so the counts
   // below are exact.
   const int n_pre = min(S - 1, n_super);
-  for (int n = 0; n < n_pre; ++n) issue(n);
+  for (int n = 0; n < n_pre; ++n) issue(n, lookup(n));
+  // the table entry of the next super-tile to issue is read one iteration
+  // ahead, so its latency hides behind a compute and a barrier
+  int phys_next = n_pre < n_super ? lookup(n_pre) : 0;
   for (int n = 0; n < n_super; ++n) {
     const int later = min(S - 2, n_super - 1 - n);  // super-tiles issued after n
     static_assert((S - 2) * RG::LOADS < 16, "vmcnt range");
@@ -342,8 +350,9 @@ prefill_mfma_kernel(PrefillArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (n + S - 1 < n_super) issue(n + S - 1);
+    if (n + S - 1 < n_super) issue(n + S - 1, phys_next);
     if (n < n_super_w) compute(n);  // wave-uniform
+    if (n + S < n_super) phys_next = lookup(n + S);
   }
 
   // normalise and store: n-tile 2u+j, row m = 4*grp + i is dim 32u + 2m + j
