@@ -208,8 +208,11 @@ def main():
     achieved = att_alg_bytes / (att_mean_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     tok_s = w.num_seqs / (ms_step * 1e-3)
+    # the kernel the library picks: matrix cores for 2..16 query heads per
+    # KV head in fp16/bf16, the vector kernel otherwise
     kernel = ("decode_vector_kernel" if w.num_heads == w.num_kv_heads
-              or w.dtype == "f32" else "decode_mfma_kernel")
+              or w.dtype == "f32" or w.num_heads // w.num_kv_heads > 16
+              else "decode_mfma_kernel")
     tag = w.name + ("_fp8" if fp8 else "")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
