@@ -226,6 +226,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, kv_bytes, fp8)
+        cpu["gpu_speedup"] = round(value / cpu["value"], 1)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
@@ -247,6 +248,7 @@ def main():
         "decode_tokens_per_s": round(tok_s, 1),
         "kernels_ms": {"reshape_and_cache": round(float(np.mean(rac_ms)), 5),
                        "attention": round(att_mean_ms, 5),
+                       "attention_median": round(float(np.median(att_ms)), 5),
                        "attention_p10": round(float(np.percentile(att_ms, 10)), 5),
                        "attention_p90": round(float(np.percentile(att_ms, 90)), 5)},
         "roofline": roofline,
@@ -417,6 +419,7 @@ def bench_prefill(args):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_prefill(w, flops)
+        cpu["gpu_speedup"] = round(flops / (ms_step * 1e-3) / 1e12 / cpu["value"], 1)
     rec = {"metric": "chunked-prefill attention TFLOP/s (causal, "
                      "4*head_dim flops per attended (token, head, key)) + "
                      "prefill tokens/s",
@@ -437,6 +440,7 @@ def bench_prefill(args):
            "prefill_tokens_per_s": round(tok_s, 1),
            "kernels_ms": {"reshape_and_cache": round(float(np.mean(rac_ms)), 5),
                           "attention": round(att_mean, 5),
+                          "attention_median": round(float(np.median(att_ms)), 5),
                           "attention_p10": round(float(np.percentile(att_ms, 10)), 5),
                           "attention_p90": round(float(np.percentile(att_ms, 90)), 5)},
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
