@@ -197,6 +197,7 @@ def main():
     log(f"[bench] {args.steps} steps in {total_ms:.2f} ms")
 
     calibration_copy(args.calib_copy_mib)
+    ceiling = read_ceiling()
 
     e = np.dtype(wl.STORAGE[w.dtype]).itemsize
     kv_bytes = w.kv_bytes(1 if fp8 else None)
@@ -252,9 +253,24 @@ def main():
                        "attention_p10": round(float(np.percentile(att_ms, 10)), 5),
                        "attention_p90": round(float(np.percentile(att_ms, 90)), 5)},
         "roofline": roofline,
+        "context": {"random_4k_tile_read_gbs": ceiling,
+                    "note": "a trivial kernel reading random 4 KiB tiles of a "
+                            "4 GiB buffer (the paged walk's access pattern, no "
+                            "arithmetic) on this GPU, for comparison with "
+                            "roofline.achieved; null if its helper is not built"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def read_ceiling():
+    """Read bandwidth of the bench_probe tile-read kernel, or None when its
+    helper library is not built."""
+    import bench_probe
+    if not os.path.exists(bench_probe.LIB):
+        log("[bench] bench_probe not built: no read ceiling")
+        return None
+    return bench_probe.random_tile_read_gbs()
 
 
 def calibration_copy(mib: int):
