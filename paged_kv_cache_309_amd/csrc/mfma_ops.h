@@ -99,16 +99,16 @@ struct MfmaTile {
 };
 
 // Two E4M3 bytes -> two 16-bit operands of type OT, exactly (every E4M3
-// value is a bfloat16 and a binary16 value).
+// value is a bfloat16 and a binary16 value, so the unit scale of CDNA4's
+// packed scaled conversion rounds nothing).  `hi` picks bytes 2-3 of w.
 template <int OT>
 __device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w, bool hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
-                     : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
   if constexpr (OT == DT_BF16) {
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
   }
 }
 

@@ -151,9 +151,13 @@ def test_cache_write_rounding_and_saturation_codes():
 
 
 @pytest.mark.parametrize("v_scale", [1.0, 0.375])
-def test_every_code_widens_exactly(v_scale):
+@pytest.mark.parametrize("qdtype,Hq", [("f32", 1), ("bf16", 8), ("f16", 8)])
+def test_every_code_widens_exactly(v_scale, qdtype, Hq):
     """One-token sequences: the output is v * v_scale exactly; 128 dims x 2
-    sequences carry all 256 codes."""
+    sequences carry all 256 codes.  An fp32 query runs the vector kernel; a
+    16-bit query with 8 query heads per KV head runs the matrix-core kernel,
+    which widens the codes to the query's type (exact for every E4M3 value,
+    and so is the product with 0.375 in both 16-bit types)."""
     import paged_kv_cache_309_amd as pkv
     S, H, D, bs = 2, 1, 128, 16
     codes = np.arange(256, dtype=np.uint8).reshape(S, D)
@@ -163,15 +167,17 @@ def test_every_code_widens_exactly(v_scale):
     for s in range(S):
         V5[s, 0, 0, :, 0] = codes[s]          # token 0 of block s
     kd, vd = fp8_pool_to_dev(kc, vc, S, H, bs, D)
-    q = torch.zeros((S, H, D), dtype=torch.float32, device="cuda")
+    q = torch.zeros((S, Hq, D), dtype=TORCH[qdtype], device="cuda")
     bt = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
     cl = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     pkv.paged_attention_decode(out, q, kd, vd, bt, cl, 0.1, v_scale=v_scale)
-    got = out.cpu().numpy().astype(np.float64)[:, 0, :]
+    got = out.float().cpu().numpy().astype(np.float64)
     want = oracle.widen(codes.reshape(-1), "fp8").reshape(S, D) * v_scale
-    assert np.array_equal(got, want.astype(np.float32).astype(np.float64),
-                          equal_nan=True)
+    for h in range(Hq):
+        assert np.array_equal(got[:, h, :],
+                              want.astype(np.float32).astype(np.float64),
+                              equal_nan=True), h
 
 
 @pytest.mark.parametrize("i", range(len(CASES)))
