@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -75,14 +76,38 @@ def parse():
     return p.parse_args()
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources; stored HBM-counter readings are used only
-    while it matches."""
-    h = hashlib.sha256()
+def source_digest(kernel: str | None = None) -> str:
+    """Hash of the sources a kernel is built from: the file that defines it,
+    the local headers it includes (transitively), the dispatcher and the
+    build flags; with no kernel named, every kernel source.  Stored
+    HBM-counter readings are used only while it matches."""
     csrc = os.path.join(ROOT, "paged_kv_cache_309_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    text = {f: open(os.path.join(csrc, f), "rb").read()
+            for f in sorted(os.listdir(csrc))}
+    if kernel is None:
+        files = sorted(text)
+    else:
+        pat = re.compile(rb"__global__[^;{]*?\b" + re.escape(kernel.encode())
+                         + rb"\s*\(", re.S)
+        files = [f for f in sorted(text) if pat.search(text[f])]
+        if not files:
+            raise ValueError(f"no kernel named {kernel} in {csrc}")
+        todo = list(files) + ["abi.hip"]
+        files = []
+        while todo:
+            f = todo.pop()
+            if f in files or f not in text:
+                continue
+            files.append(f)
+            todo += [m.decode() for m in
+                     re.findall(rb'#include "([^"]+)"', text[f])]
+        files.sort()
+    h = hashlib.sha256()
+    for f in files:
+        h.update(f.encode() + text[f])
+    with open(os.path.join(ROOT, "paged_kv_cache_309_amd", "build.py"),
+              "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -94,7 +119,7 @@ def stored_traffic(kernel: str, workload: str):
         rec = json.load(open(path)).get(f"{kernel}:{workload}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != source_digest():
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 

@@ -1,0 +1,51 @@
+"""Host-side pieces of bench.py: the per-kernel source digest that keys the
+stored HBM-counter readings, and the refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNELS = ["decode_vector_kernel", "decode_mfma_kernel", "prefill_mfma_kernel",
+           "copy_blocks_kernel", "partition_reduce_kernel",
+           "reshape_and_cache_kernel", "reshape_and_cache_fp8_kernel"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_every_kernel_has_a_digest(kernel):
+    d = bench.source_digest(kernel)
+    assert len(d) == 16 and d == bench.source_digest(kernel)
+
+
+def test_digests_separate_kernels_in_different_files():
+    assert bench.source_digest("decode_vector_kernel") != \
+        bench.source_digest("prefill_mfma_kernel")
+    # two kernels of one file share the file's digest
+    assert bench.source_digest("reshape_and_cache_kernel") == \
+        bench.source_digest("partition_reduce_kernel")
+
+
+def test_unknown_kernel_is_an_error():
+    with pytest.raises(ValueError):
+        bench.source_digest("no_such_kernel")
+
+
+def test_stored_traffic_keys_name_real_kernels():
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        pytest.skip("no stored counter readings")
+    for key in json.load(open(path)):
+        kernel, workload = key.split(":")
+        bench.source_digest(kernel)          # raises if the kernel is gone
+        assert workload
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
