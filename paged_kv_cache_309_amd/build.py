@@ -40,6 +40,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file additions.  The matrix-core prefill's softmax maxima never see a
+# NaN (logits of masked and out-of-context tokens are set to -inf before the
+# maximum, and values past the context are zeroed bitwise), so its compile
+# may drop the NaN quieting around every max: about 18 fewer vector
+# instructions per 32-token step.  Infinities are still honoured.
+FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -57,7 +65,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

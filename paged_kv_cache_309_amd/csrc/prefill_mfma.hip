@@ -226,32 +226,29 @@ prefill_mfma_kernel(PrefillArgs a) {
   auto compute = [&](int n) {
     const char *base = ring + (n % S) * RG::TILE;
     const bool diag = 32 * n + 31 > pos_first;
-    u32x4 kop[2][KC], vop[2][NC];
+    // K operands of both tiles first: the logit products wait only for them,
+    // and the value reads complete while those products run
+    u32x4 kop[2][KC];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
         const int c = kk * 4 + grp;
         kop[st][kk] = lds16(base + st * RG::PIECE + col * 2 * D + ((c ^ (col % RG::CR)) * 16));
       }
+    // value operand of n-tile 2u+j: dim 32u + 2*col + j, four tokens of tile
+    // 0 then the same four of tile 1 (8 bytes each, one piece apart, so one
+    // two-address LDS read fills the operand's registers in place)
+    u32x4 va[NT];
 #pragma unroll
-      for (int u = 0; u < NC; ++u)
-        vop[st][u] = lds16(base + (2 + st) * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8);
-      const int t0 = 32 * n + 16 * st + 4 * grp;
-      if (32 * n + 16 * st + 16 > L) {
-        // tokens at or past L may hold anything (NaN included): zero them
-        const int nvalid = max(0, min(4, L - t0));
-        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+    for (int u = 0; u < NC; ++u)
 #pragma unroll
-        for (int u = 0; u < NC; ++u) {
-          vop[st][u][0] &= m01;
-          vop[st][u][1] &= m23;
-          vop[st][u][2] &= m01;
-          vop[st][u][3] &= m23;
-        }
+      for (int j = 0; j < 2; ++j) {
+        const char *v0 = base + 2 * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8 + 8 * j;
+        const u32x2 lo = *(const volatile __attribute__((address_space(3))) u32x2 *)v0;
+        const u32x2 hi = *(const volatile __attribute__((address_space(3))) u32x2 *)(v0 + RG::PIECE);
+        va[2 * u + j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-    }
     // logits of both row tiles first, so that one tile's softmax can run on
     // the vector ALUs while the other's products are still in the matrix
     // cores
@@ -276,6 +273,20 @@ prefill_mfma_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i)
             if (t0 + i > pos[qt]) x[qt][st][i] = -INFINITY;
         }
+    }
+    if (32 * n + 32 > L) {
+      // tokens at or past L may hold anything (NaN included): zero their values
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int nvalid = max(0, min(4, L - (32 * n + 16 * st + 4 * grp)));
+        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          va[t][2 * st] &= m01;
+          va[t][2 * st + 1] &= m23;
+        }
+      }
     }
     // running maxima (base-2 units), moved only when a logit exceeds one by
     // more than the slack somewhere in the wave: one test for all row tiles
@@ -314,14 +325,7 @@ prefill_mfma_kernel(PrefillArgs a) {
       const u32x4 pb = {Ops::pack2(p[0][0], p[0][1]), Ops::pack2(p[0][2], p[0][3]),
                         Ops::pack2(p[1][0], p[1][1]), Ops::pack2(p[1][2], p[1][3])};
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4 va = {vop[0][u][2 * j], vop[0][u][2 * j + 1], vop[1][u][2 * j],
-                            vop[1][u][2 * j + 1]};
-          acc[qt][2 * u + j] = Ops::pv32(va, pb, acc[qt][2 * u + j]);
-        }
-      }
+      for (int t = 0; t < NT; ++t) acc[qt][t] = Ops::pv32(va[t], pb, acc[qt][t]);
       lsum[qt] = Ops::pv32(ones, pb, lsum[qt]);  // every row: the sum of the weights
     }
   };
