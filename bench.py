@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import importlib.util
 import re
 import json
 import os
@@ -78,8 +79,8 @@ def parse():
 
 def source_digest(kernel: str | None = None) -> str:
     """Hash of the sources a kernel is built from: the file that defines it,
-    the local headers it includes (transitively), the dispatcher and the
-    build flags; with no kernel named, every kernel source.  Stored
+    the local headers it includes (transitively), the dispatcher, and each
+    file's compile flags; with no kernel named, every kernel source.  Stored
     HBM-counter readings are used only while it matches."""
     csrc = os.path.join(ROOT, "paged_kv_cache_309_amd", "csrc")
     text = {f: open(os.path.join(csrc, f), "rb").read()
@@ -102,12 +103,17 @@ def source_digest(kernel: str | None = None) -> str:
             todo += [m.decode() for m in
                      re.findall(rb'#include "([^"]+)"', text[f])]
         files.sort()
+    # the build script by path: no need to load the library for its flags
+    spec = importlib.util.spec_from_file_location(
+        "pkv_build_flags", os.path.join(ROOT, "paged_kv_cache_309_amd", "build.py"))
+    build_mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build_mod)
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode() + text[f])
-    with open(os.path.join(ROOT, "paged_kv_cache_309_amd", "build.py"),
-              "rb") as fh:
-        h.update(fh.read())
+        # the compile line of this file (the flags every file gets, plus its own)
+        flags = build_mod.HIPCC_FLAGS + build_mod.FILE_FLAGS.get(f, [])
+        h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
