@@ -237,7 +237,10 @@ __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mi
 // The same walk with NBUF - 1 tiles in flight while one is computed
 // (NBUF buffers in rotation): for small tiles (8-bit caches), where one
 // tile of lookahead leaves too few bytes in flight per wavefront to cover
-// the memory latency.
+// the memory latency.  Block-table entries are read here with scalar
+// loads, one tile ahead: they count on their own counter, so the wait
+// before a compute can leave all later tiles' loads outstanding (a vector
+// load of entries, as in walk_tiles, would make that wait drain them).
 template <class Tile, int NBUF, int STRIDE = 4, class Load, class Compute>
 __device__ __forceinline__ void walk_tiles_n(const int32_t *trow, int k0, int n_mine,
                                              int subs, unsigned num_blocks,
@@ -245,37 +248,56 @@ __device__ __forceinline__ void walk_tiles_n(const int32_t *trow, int k0, int n_
                                              size_t block_bytes, size_t sub_bytes,
                                              Load load, Compute compute) {
   static_assert(NBUF >= 2, "at least two buffers");
-  const int lane = threadIdx.x & 63;
-  auto fetch = [&](int n0) -> int {
-    const int n = n0 + lane;
-    return n < n_mine ? trow[(k0 + STRIDE * n) / subs] : 0;
-  };
-  // table entries of tiles [cur_base, cur_base + 64) are in ent_cur, the
-  // next 64 in ent_nxt; offset_of is called with n increasing by one
-  int ent_cur = fetch(0);
-  int ent_nxt = n_mine > 64 ? fetch(64) : 0;
-  int cur_base = 0;
-  auto offset_of = [&](int n) -> size_t {
-    if (n - cur_base >= 64) {
-      ent_cur = ent_nxt;
-      cur_base += 64;
-      if (cur_base + 64 < n_mine) ent_nxt = fetch(cur_base + 64);
-    }
-    int phys = __builtin_amdgcn_readlane(ent_cur, n - cur_base);
+  const __attribute__((address_space(4))) int32_t *tr =
+      (const __attribute__((address_space(4))) int32_t *)trow;
+  auto entry = [&](int n) -> int { return tr[(k0 + STRIDE * n) / subs]; };
+  auto offset_of = [&](int n, int phys) -> size_t {
     phys = (unsigned)phys < num_blocks ? phys : 0;
     const int k = k0 + STRIDE * n;
     return (size_t)phys * block_bytes + head_off_bytes + (size_t)(k % subs) * sub_bytes;
   };
-  // invariant at the top of the loop: t[b] holds tile n + b, b < NBUF - 1
+  // invariant at the top of each loop: t[b] holds tile n + b, b < NBUF - 1,
+  // and phys_next is the entry of tile n + NBUF - 1
   Tile t[NBUF];
+  int n = 0, phys_next = 0;
+  if (n_mine > 2 * NBUF - 2) {
+    // a walk long enough for the steady state: nothing before it is
+    // conditional either, so the waits there leave exactly the later
+    // tiles' loads outstanding (a load that may or may not have been
+    // issued makes the compiler count conservatively, draining them)
+    // in tile order (a scheduling barrier after each tile keeps the
+    // compiler from reordering the loads, which would make the first
+    // compute wait for all of them)
 #pragma unroll
-  for (int b = 0; b < NBUF - 1; ++b)
-    if (b < n_mine) load(t[b], offset_of(b));
-  int n = 0;
+    for (int b = 0; b < NBUF - 1; ++b) {
+      load(t[b], offset_of(b, entry(b)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    phys_next = entry(NBUF - 1);
+    for (; n + 2 * NBUF - 2 < n_mine; n += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        const int nl = n + b + NBUF - 1;  // the tile loaded in this step
+        load(t[(b + NBUF - 1) % NBUF], offset_of(nl, phys_next));
+        if (nl + 1 < n_mine) phys_next = entry(nl + 1);
+        compute(t[b], n + b);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b)
+      if (b < n_mine) load(t[b], offset_of(b, entry(b)));
+    phys_next = NBUF - 1 < n_mine ? entry(NBUF - 1) : 0;
+  }
+  // the last round (at most one), with the loads guarded
   for (; n + NBUF - 1 < n_mine; n += NBUF) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
-      if (n + b + NBUF - 1 < n_mine) load(t[(b + NBUF - 1) % NBUF], offset_of(n + b + NBUF - 1));
+      const int nl = n + b + NBUF - 1;
+      if (nl < n_mine) {
+        load(t[(b + NBUF - 1) % NBUF], offset_of(nl, phys_next));
+        if (nl + 1 < n_mine) phys_next = entry(nl + 1);
+      }
       compute(t[b], n + b);
     }
   }
