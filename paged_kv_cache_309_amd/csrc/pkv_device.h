@@ -189,49 +189,54 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
 // Walks the 16-token tiles a wavefront owns, with one tile of prefetch.
 //
 // The wave owns tiles k = k0 + STRIDE*n, n = 0 .. n_mine-1 (decode: k0 =
-// first tile of the range + wave index, STRIDE = 4 waves; prefill: every
-// tile, STRIDE = 1); tile k lives in block table entry k / subs, at token
-// offset 16 * (k % subs) of that block.  Block-table entries are fetched
-// 64 at a time, one per lane, and broadcast with readlane, so the byte
-// offset of every tile is a wave-uniform (scalar) value.
+// first tile of the range + wave index, STRIDE = 4 waves); tile k lives in
+// block table entry k / subs, at token offset 16 * (k % subs) of that
+// block.  Entries are wave-uniform and read with scalar loads, one tile
+// ahead of their use; they count on their own counter, apart from the
+// tiles' vector loads.
 //
 //   load(tile, byte_offset)  issues the loads of one tile
 //   compute(tile, n)         consumes the n-th tile
 //
-// Two tile buffers alternate (no register copies between iterations).
+// Two tile buffers alternate (no register copies between iterations).  In
+// the steady state no load is conditional, so the wait before each compute
+// leaves the next tile's loads outstanding: a load that may or may not have
+// been issued makes the compiler count conservatively and drain it.
+// n_mine >= 1.
 template <class Tile, int STRIDE = 4, class Load, class Compute>
 __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mine,
                                            int subs, unsigned num_blocks,
                                            size_t head_off_bytes,
                                            size_t block_bytes, size_t sub_bytes,
                                            Load load, Compute compute) {
-  const int lane = threadIdx.x & 63;
-  auto fetch = [&](int n0) -> int {
-    const int n = n0 + lane;
-    return n < n_mine ? trow[(k0 + STRIDE * n) / subs] : 0;
-  };
-  int ent_cur = fetch(0);
-  int ent_nxt = n_mine > 64 ? fetch(64) : 0;
-  auto offset_of = [&](int n) -> size_t {
-    if ((n & 63) == 0 && n > 0) {
-      ent_cur = ent_nxt;
-      if (n + 64 < n_mine) ent_nxt = fetch(n + 64);
-    }
-    int phys = __builtin_amdgcn_readlane(ent_cur, n & 63);
+  const __attribute__((address_space(4))) int32_t *tr =
+      (const __attribute__((address_space(4))) int32_t *)trow;
+  auto entry = [&](int n) -> int { return tr[(k0 + STRIDE * n) / subs]; };
+  auto offset_of = [&](int n, int phys) -> size_t {
     phys = (unsigned)phys < num_blocks ? phys : 0;
     const int k = k0 + STRIDE * n;
     return (size_t)phys * block_bytes + head_off_bytes + (size_t)(k % subs) * sub_bytes;
   };
   Tile ta, tb;
-  load(ta, offset_of(0));
+  load(ta, offset_of(0, entry(0)));
+  int phys_next = 1 < n_mine ? entry(1) : 0;  // entry of the next tile to load
   int n = 0;
-  for (; n + 1 < n_mine; n += 2) {
-    load(tb, offset_of(n + 1));
+  for (; n + 2 < n_mine; n += 2) {
+    load(tb, offset_of(n + 1, phys_next));
+    phys_next = entry(n + 2);
     compute(ta, n);
-    if (n + 2 < n_mine) load(ta, offset_of(n + 2));
+    load(ta, offset_of(n + 2, phys_next));
+    if (n + 3 < n_mine) phys_next = entry(n + 3);
     compute(tb, n + 1);
   }
-  if (n < n_mine) compute(ta, n);
+  // one or two tiles left; ta holds tile n
+  if (n + 1 < n_mine) {
+    load(tb, offset_of(n + 1, phys_next));
+    compute(ta, n);
+    compute(tb, n + 1);
+  } else {
+    compute(ta, n);
+  }
 }
 
 // The same walk with NBUF - 1 tiles in flight while one is computed
