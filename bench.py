@@ -77,10 +77,37 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(src: bytes) -> bytes:
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that an edit of a comment leaves a kernel's digest unchanged.  String
+    and character literals are kept as they are."""
+    out, i, n = bytearray(), 0, len(src)
+    while i < n:
+        c = src[i:i + 1]
+        if c in (b'"', b"'"):
+            j = i + 1
+            while j < n and src[j:j + 1] != c:
+                j += 2 if src[j:j + 1] == b"\\" else 1
+            out += src[i:j + 1]
+            i = j + 1
+        elif src.startswith(b"//", i):
+            j = src.find(b"\n", i)
+            i = n if j < 0 else j
+        elif src.startswith(b"/*", i):
+            j = src.find(b"*/", i + 2)
+            i = n if j < 0 else j + 2
+            out += b" "
+        else:
+            out += c
+            i += 1
+    return b" ".join(bytes(out).split())
+
+
 def source_digest(kernel: str | None = None) -> str:
-    """Hash of the sources a kernel is built from: the file that defines it,
-    the local headers it includes (transitively), the dispatcher, and each
-    file's compile flags; with no kernel named, every kernel source.  Stored
+    """Hash of the code a kernel is built from (comments and layout left
+    out): the file that defines it, the local headers it includes
+    (transitively), the dispatcher, and each file's compile flags; with no
+    kernel named, every kernel source.  Stored
     HBM-counter readings are used only while it matches."""
     csrc = os.path.join(ROOT, "paged_kv_cache_309_amd", "csrc")
     text = {f: open(os.path.join(csrc, f), "rb").read()
@@ -110,7 +137,7 @@ def source_digest(kernel: str | None = None) -> str:
     spec.loader.exec_module(build_mod)
     h = hashlib.sha256()
     for f in files:
-        h.update(f.encode() + text[f])
+        h.update(f.encode() + _code_only(text[f]))
         # the compile line of this file (the flags every file gets, plus its own)
         flags = build_mod.HIPCC_FLAGS + build_mod.FILE_FLAGS.get(f, [])
         h.update(" ".join(flags).encode())

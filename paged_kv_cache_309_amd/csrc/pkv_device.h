@@ -240,12 +240,10 @@ __device__ __forceinline__ void walk_tiles(const int32_t *trow, int k0, int n_mi
 }
 
 // The same walk with NBUF - 1 tiles in flight while one is computed
-// (NBUF buffers in rotation): for small tiles (8-bit caches), where one
-// tile of lookahead leaves too few bytes in flight per wavefront to cover
-// the memory latency.  Block-table entries are read here with scalar
-// loads, one tile ahead: they count on their own counter, so the wait
-// before a compute can leave all later tiles' loads outstanding (a vector
-// load of entries, as in walk_tiles, would make that wait drain them).
+// (NBUF buffers in rotation), for the matrix-core kernel: two tiles of
+// lookahead for 16-bit caches, three for the 2 KiB tiles of 8-bit caches.
+// Block-table entries are read with scalar loads one tile ahead, as in
+// walk_tiles.
 template <class Tile, int NBUF, int STRIDE = 4, class Load, class Compute>
 __device__ __forceinline__ void walk_tiles_n(const int32_t *trow, int k0, int n_mine,
                                              int subs, unsigned num_blocks,

@@ -49,3 +49,13 @@ def test_more_than_one_gpu_is_refused():
                         "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_digest_ignores_comments_not_code():
+    a = b"int f(int x) { return x + 1; } // one\n/* two */"
+    b = b"int f(int x) {\n  return x + 1;  // changed comment\n}"
+    c = b"int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    # a comment marker inside a string literal is code
+    assert b"//" in bench._code_only(b'const char *u = "a//b";')
