@@ -12,36 +12,72 @@ namespace pkv {
 // the same rescaling the online softmax uses inside a partition, so the
 // result is the softmax over the whole context.  Partitions at or past
 // ceil(L / part_tokens) were empty and are not read.
-// One workgroup of D threads per (sequence, head).
+// One workgroup of 256 threads per (sequence, head): thread t takes the
+// four dims 4 (t % (D/4)) .. +3 of the partitions p = t / (D/4) (mod
+// 256 / (D/4)), as 16-byte loads of o_p; the partial sums of the partition
+// groups are added through LDS.
+constexpr int kReduceThreads = 256;
+
 template <int DT, int D>
-__global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+__global__ void __launch_bounds__(kReduceThreads) partition_reduce_kernel(DecodeArgs a) {
+  constexpr int Q = D / 4;                 // dim quads per row
+  constexpr int PG = kReduceThreads / Q;   // partition groups
+  constexpr int W = kReduceThreads / 64;   // wavefronts
+  __shared__ f32x4 sm_num[PG][Q];
+  __shared__ float sm_den[PG];
+  __shared__ float sm_max[W];
+  const int h = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int q = t % Q, pg = t / Q;
   const int Hq = a.num_heads;
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks * a.block_size));
   const int np = min(a.num_parts, (L + a.part_tokens - 1) / a.part_tokens);
   const size_t base = ((size_t)s * Hq + h) * a.num_parts;
   const size_t orow = ((size_t)s * Hq + h) * D;
-  if (np <= 0) {
-    store_elem<DT>(a.out, orow + d, 0.f);
+  if (np <= 0) {  // the whole workgroup
+    for (int i = t; i < D; i += kReduceThreads) store_elem<DT>(a.out, orow + i, 0.f);
     return;
   }
+  // M = max_p m_p: a strided slice per thread, then the workgroup maximum
   float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[base + p]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < np; ++p) {
+  for (int p = t; p < np; p += kReduceThreads) M = fmaxf(M, a.ws_m[base + p]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((t & 63) == 0) sm_max[t >> 6] = M;
+  __syncthreads();
+  M = sm_max[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) M = fmaxf(M, sm_max[i]);
+  // this thread's partitions
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int p = pg; p < np; p += PG) {
     const float f = fast_exp2(a.ws_m[base + p] - M);
-    num = fmaf(f, a.ws_o[(base + p) * D + d], num);
+    const f32x4 o = *reinterpret_cast<const f32x4 *>(a.ws_o + (base + p) * D + 4 * q);
+    num += f * o;
     den = fmaf(f, a.ws_l[base + p], den);
   }
-  store_elem<DT>(a.out, orow + d, num / den);
+  sm_num[pg][q] = num;
+  if (q == 0) sm_den[pg] = den;
+  __syncthreads();
+  if (pg == 0) {
+    f32x4 n = sm_num[0][q];
+    float dd = sm_den[0];
+#pragma unroll
+    for (int i = 1; i < PG; ++i) {
+      n += sm_num[i][q];
+      dd += sm_den[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_elem<DT>(a.out, orow + 4 * q + e, n[e] / dd);
+  }
 }
 
 hipError_t launch_partition_reduce(const DecodeArgs &a, int dtype,
                                    int head_dim, hipStream_t st) {
   dim3 grid(a.num_heads, a.num_seqs);
 #define PKV_REDUCE(DTV, DV) \
-  hipLaunchKernelGGL((partition_reduce_kernel<DTV, DV>), grid, dim3(DV), 0, st, a)
+  hipLaunchKernelGGL((partition_reduce_kernel<DTV, DV>), grid, dim3(kReduceThreads), 0, st, a)
   if (head_dim == 128) {
     if (dtype == DT_F32) PKV_REDUCE(DT_F32, 128);
     else if (dtype == DT_F16) PKV_REDUCE(DT_F16, 128);
