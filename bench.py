@@ -160,8 +160,8 @@ def stored_traffic(kernel: str, workload: str):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every box here has one GPU); run it with --gpus 1",
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
+              "run it with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

@@ -28,7 +28,7 @@ what the pages say the manager does:
     host-side pool of blocks; every block they hold moves once, keeping its
     sharers.
 
-Conventions this build fixes (the pages leave them open): the free list is
+Conventions fixed here (the pages leave them open): the free list is
 a stack whose initial order hands out blocks 0, 1, 2, ...; a finished
 sequence returns its blocks in reverse table order; a batch of appends is
 served in order and either succeeds whole or changes nothing.  A swap moves
