@@ -47,6 +47,23 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
+def _on_one_device(*tensors: torch.Tensor, stream=None) -> None:
+    """The kernels dereference these pointers on the GPU: every tensor must
+    be a CUDA tensor, all on one device, the device the launch goes to (the
+    given stream's, else the current one)."""
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"libpkv needs CUDA tensors; got one on {t.device}")
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"libpkv needs all tensors on one device; got {dev} and {t.device}")
+    launch = stream.device if stream is not None else \
+        torch.device("cuda", torch.cuda.current_device())
+    if dev != launch:
+        raise ValueError(f"tensors are on {dev} but the launch goes to {launch}")
+
+
 def _dtype(t: torch.Tensor) -> int:
     try:
         return _DTYPES[t.dtype]
@@ -86,6 +103,7 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor,
                       k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Write k[i], v[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64);
     8-bit caches store the E4M3 value nearest to x / scale."""
+    _on_one_device(k, v, k_cache, v_cache, slot_mapping, stream=stream)
     T, Hkv, D = k.shape
     NB, bs = k_cache.shape[0], k_cache.shape[2]
     dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k))
@@ -109,6 +127,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor,
                            v_scale: float = 1.0) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K) V over context_lens[s]
     tokens reached through block_tables[s]; single launch."""
+    _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens, stream=stream)
     bs = block_size or k_cache.shape[2]
     dims = _dims(q, k_cache, block_tables)
     if _is_fp8(k_cache):
@@ -148,6 +167,8 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
     """Same result as paged_attention_decode, in two launches: per-partition
     partials into `workspace` (a device byte tensor of at least
     split_workspace_bytes(...)), then the partition reduce."""
+    _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens, workspace,
+                   stream=stream)
     bs = block_size or k_cache.shape[2]
     dims = _dims(q, k_cache, block_tables)
     if _is_fp8(k_cache):
@@ -179,6 +200,8 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor,
     sequence (rows query_start_loc[s] .. query_start_loc[s+1]-1, the last
     tokens of its context, whose K/V are already in the cache); each
     attends causally.  max_query_len bounds every chunk (default T)."""
+    _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens,
+                   query_start_loc, stream=stream)
     T = q.shape[0]
     bs = block_size or k_cache.shape[2]
     S = context_lens.shape[0]
@@ -204,6 +227,8 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
                 block_mapping: torch.Tensor, stream=None) -> None:
     """Copy-on-write: block block_mapping[i, 1] of both caches becomes a
     copy of block block_mapping[i, 0] (device int64 [n, 2])."""
+    _on_one_device(k_cache, v_cache, *([block_mapping] if block_mapping.numel() else []),
+                   stream=stream)
     NB, Hkv, bs, D = k_cache.shape
     dt = _lib.PKV_E4M3 if _is_fp8(k_cache) else _dtype(k_cache)
     dims = PkvDims(0, Hkv, Hkv, D, NB, 0, dt)

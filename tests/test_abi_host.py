@@ -199,3 +199,31 @@ def test_prefill_rejects_bad_arguments():
     assert pf(d, qsl=A + 64) == ERR["PKV_ERR_ALIAS"]
     assert pf(d, T=0, out=None, q=None) == 0
     assert pf(dims(S_=0), out=None) == 0
+
+
+def test_python_binding_refuses_host_tensors():
+    """The kernels dereference every pointer on the GPU: the binding turns a
+    CPU tensor into a ValueError before any launch."""
+    import torch
+    import paged_kv_cache_309_amd as pkv
+    S, H, D, NB, bs = 2, 2, 64, 4, 16
+    q = torch.zeros(S, H, D, dtype=torch.float16)
+    out = torch.empty_like(q)
+    kc = torch.zeros(NB, H, bs, D, dtype=torch.float16)
+    vc = torch.zeros(NB, H, bs // 4, D, 4, dtype=torch.float16)
+    bt = torch.zeros(S, 2, dtype=torch.int32)
+    cl = torch.ones(S, dtype=torch.int32)
+    qsl = torch.tensor([0, 1, 2], dtype=torch.int32)
+    slots = torch.zeros(S, dtype=torch.int64)
+    ws = torch.empty(1 << 16, dtype=torch.uint8)
+    mapping = torch.zeros(1, 2, dtype=torch.int64)
+    calls = [
+        lambda: pkv.reshape_and_cache(q, q, kc, vc, slots),
+        lambda: pkv.paged_attention_decode(out, q, kc, vc, bt, cl, 0.1),
+        lambda: pkv.paged_attention_decode_split(out, q, kc, vc, bt, cl, 0.1, 16, ws),
+        lambda: pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, 0.1),
+        lambda: pkv.copy_blocks(kc, vc, mapping),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="CUDA tensors"):
+            call()
