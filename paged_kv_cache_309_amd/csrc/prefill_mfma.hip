@@ -50,6 +50,8 @@
 // it adds exactly the rounded weights the value product applied, and the
 // softmax stays off the vector ALUs as far as possible: per logit one fused
 // multiply-add and one exp2, plus the running maximum.  Accumulation is fp32.
+#include <type_traits>
+
 #include "mfma_ops.h"
 
 namespace pkv {
@@ -201,10 +203,10 @@ prefill_mfma_kernel(PrefillArgs a) {
     return (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
   };
   // wavefront w fills piece w of super-tile n into stage n % S
-  auto issue = [&](int n, int phys) {
+  auto issue = [&](int n, int phys, int stage) {
     const int tb = 32 * n + 16 * (w & 1);
     const char *src = src_base + phys * block_bytes + (size_t)(tb % BS) * D * 2;
-    char *dst = ring + (n % S) * RG::TILE + w * RG::PIECE;
+    char *dst = ring + stage * RG::TILE + w * RG::PIECE;
 #pragma unroll
     for (int b = 0; b < RG::LOADS; ++b)
       load_lds16(src + lane_off[b], dst + b * 1024);
@@ -223,8 +225,10 @@ prefill_mfma_kernel(PrefillArgs a) {
   const uint32_t one2 = Ops::pack2(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
 
-  auto compute = [&](int n) {
-    const char *base = ring + (n % S) * RG::TILE;
+  // stage = n % S; MAY_TAIL: the super-tile may reach past L
+  auto compute = [&](int n, int stage, auto may_tail) {
+    constexpr bool MAY_TAIL = decltype(may_tail)::value;
+    const char *base = ring + stage * RG::TILE;
     const bool diag = 32 * n + 31 > pos_first;
     // K operands of both tiles first: the logit products wait only for them,
     // and the value reads complete while those products run
@@ -274,7 +278,7 @@ prefill_mfma_kernel(PrefillArgs a) {
             if (t0 + i > pos[qt]) x[qt][st][i] = -INFINITY;
         }
     }
-    if (32 * n + 32 > L) {
+    if (MAY_TAIL && 32 * n + 32 > L) {
       // tokens at or past L may hold anything (NaN included): zero their values
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -337,27 +341,46 @@ prefill_mfma_kernel(PrefillArgs a) {
   // the stage super-tile n - 1 used, and computes on super-tile n.  Every
   // super-tile costs each wavefront exactly RG::LOADS loads, so the counts
   // below are exact.
+  static_assert((S - 2) * RG::LOADS < 16, "vmcnt range");
   const int n_pre = min(S - 1, n_super);
-  for (int n = 0; n < n_pre; ++n) issue(n, lookup(n));
+  for (int n = 0; n < n_pre; ++n) issue(n, lookup(n), n);
   // the table entry of the next super-tile to issue is read one iteration
   // ahead, so its latency hides behind a compute and a barrier
   int phys_next = n_pre < n_super ? lookup(n_pre) : 0;
-  for (int n = 0; n < n_super; ++n) {
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  int n = 0;
+  // steady state, S iterations per trip while at least 2 S super-tiles
+  // remain: every iteration leaves S - 2 later super-tiles in flight,
+  // refills a stage, reads one entry ahead, and ends at least 32 tokens
+  // before L (no tail mask); the stages are constants
+  for (; n + 2 * S <= n_super; n += S) {
+#pragma unroll
+    for (int b = 0; b < S; ++b) {
+      wait_vm<(S - 2) * RG::LOADS>();
+      barrier();
+      issue(n + b + S - 1, phys_next, (b + S - 1) % S);
+      if (n + b < n_super_w) compute(n + b, b, std::false_type{});  // wave-uniform
+      phys_next = lookup(n + b + S);
+    }
+  }
+  for (; n < n_super; ++n) {
     const int later = min(S - 2, n_super - 1 - n);  // super-tiles issued after n
-    static_assert((S - 2) * RG::LOADS < 16, "vmcnt range");
     if (later >= 2)
       wait_vm<2 * RG::LOADS>();
     else if (later == 1)
       wait_vm<RG::LOADS>();
     else
       wait_vm<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (n + S - 1 < n_super) issue(n + S - 1, phys_next);
-    if (n < n_super_w) compute(n);  // wave-uniform
+    barrier();
+    if (n + S - 1 < n_super) issue(n + S - 1, phys_next, (n + S - 1) % S);
+    if (n < n_super_w) compute(n, n % S, std::true_type{});  // wave-uniform
     if (n + S < n_super) phys_next = lookup(n + S);
   }
+  static_assert(S == 4, "the general loop's waits cover S - 2 = 2 later super-tiles");
 
   // normalise and store: n-tile 2u+j, row m = 4*grp + i is dim 32u + 2m + j
   // of the lane's query row; the two n-tiles of a chunk give two adjacent
