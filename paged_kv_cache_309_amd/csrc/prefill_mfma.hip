@@ -198,14 +198,17 @@ prefill_mfma_kernel(PrefillArgs a) {
   // physical block of this wavefront's piece of super-tile n (a tile past
   // the context: any block, its contents are masked)
   auto lookup = [&](int n) -> int {
-    const int tb = 32 * n + 16 * (w & 1);
-    const int phys = tb < L ? trow[tb / BS] : 0;
+    const unsigned tb = 32u * n + 16u * (w & 1);
+    const int phys = tb < (unsigned)L ? trow[tb / BS] : 0;
     return (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
   };
   // wavefront w fills piece w of super-tile n into stage n % S
   auto issue = [&](int n, int phys, int stage) {
-    const int tb = 32 * n + 16 * (w & 1);
-    const char *src = src_base + phys * block_bytes + (size_t)(tb % BS) * D * 2;
+    const unsigned tb = 32u * n + 16u * (w & 1);
+    // phys is in [0, num_blocks) and a block is far below 4 GiB: an unsigned
+    // 32 x 32 -> 64-bit product
+    const char *src = src_base + (uint64_t)(unsigned)phys * (unsigned)block_bytes +
+                      (tb % BS) * D * 2;
     char *dst = ring + stage * RG::TILE + w * RG::PIECE;
 #pragma unroll
     for (int b = 0; b < RG::LOADS; ++b)
