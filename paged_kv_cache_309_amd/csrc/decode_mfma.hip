@@ -27,7 +27,12 @@
 //    mapped to dim 32*u + 2*m + j for n-tile 2*u + j, so that every lane's
 //    A operands of two consecutive n-tiles are one 16-byte chunk of the V
 //    tile, and one load instruction covers four 256-byte runs;
-//  * heads >= G are padding columns, masked to -inf.
+//  * heads >= G are padding columns, masked to -inf;
+//  * an 8-bit K tile with 128-byte rows is loaded as whole rows: load c,
+//    lane (col, grp) reads token 8c + col%8, 16-byte chunk 2*grp + col/8;
+//    one DPP move per dword then gives lane (col, grp) token col's chunks
+//    2*grp and 2*grp+1 (dims 32*grp .. 32*grp+31).  Loads that each cover
+//    half of sixteen rows read the 8-bit cache about 5% slower on MI355X.
 //
 // The probabilities enter the value product as a high and a low
 // half-precision part (p = hi + lo to about 16 significant bits), so the
@@ -36,6 +41,16 @@
 #include "mfma_ops.h"
 
 namespace pkv {
+
+// Half-row exchange: in each row of 16 lanes, the lanes that BANKS enables
+// (bit i: lanes 4i..4i+3 of the row) take `src` from lane l ^ 8 (DPP
+// row_ror:8), the others keep `old`.  One DPP move.
+template <int BANKS>
+__device__ __forceinline__ uint32_t from_other_half(uint32_t old, uint32_t src) {
+  constexpr int kRowRor8 = 0x128;
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(src), kRowRor8, 0xF, BANKS, false));
+}
 
 // QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
 template <int QT, int CT, int D, int BS, bool SPLIT>
@@ -47,6 +62,7 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int E = Elem<CT>::bytes;  // cache element bytes
   constexpr int KC = D / 32;          // logit MFMAs per tile
   constexpr int NT = D / 16;          // value n-tiles
+  constexpr bool KW = F8 && D == 128; // K loaded as whole rows, then exchanged
 
   const int g = blockIdx.x, part = blockIdx.z;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
@@ -80,13 +96,13 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // Q^T operand: lane holds head `col` and the eight dims the K operand of
   // logit MFMA kk holds in this lane: (kk*4+grp)*8 for 16-bit caches,
-  // (kk/2)*64 + grp*16 + (kk%2)*8 for 8-bit caches
+  // 32*grp + 8*kk (D = 128) or 16*grp + 8*kk (D = 64) for 8-bit caches
   u32x4 qop[KC];
   {
     const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * 2;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
-      const int d0 = F8 ? (kk / 2) * 64 + grp * 16 + (kk % 2) * 8 : (kk * 4 + grp) * 8;
+      const int d0 = F8 ? (KW ? 32 : 16) * grp + 8 * kk : (kk * 4 + grp) * 8;
       qop[kk] = col < G ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
                         : u32x4{0u, 0u, 0u, 0u};
     }
@@ -101,9 +117,11 @@ decode_mfma_kernel(DecodeArgs a) {
   const int n_tiles = st_end - st_begin;
   const int n_mine = n_tiles > w ? (n_tiles - w + 3) >> 2 : 0;
 
-  // lane offsets inside a tile, in bytes (chunk c adds c*64 for K, c*256
-  // for V): K row `col`, V token group `grp`
-  const uint32_t koff = (uint32_t)(col * D * E + grp * 16);
+  // lane offsets inside a tile, in bytes (chunk c adds KSTEP*c for K, 256*c
+  // for V): K row `col` (8-bit, D = 128: row 8c + col%8), V token group `grp`
+  const uint32_t koff = KW ? (uint32_t)((col % 8) * D + (2 * grp + col / 8) * 16)
+                           : (uint32_t)(col * D * E + grp * 16);
+  constexpr int KSTEP = KW ? 8 * D : 64;
   const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);
 
   float m = -INFINITY, l = 0.f;  // head `col`; l is this lane's share
@@ -115,7 +133,7 @@ decode_mfma_kernel(DecodeArgs a) {
     const char *kp = kc + tile_bytes + koff;
     const char *vp = vc + tile_bytes + voff;
 #pragma unroll
-    for (int c = 0; c < Tl::NC; ++c) t.k[c] = load_stream16(kp + c * 64);
+    for (int c = 0; c < Tl::NC; ++c) t.k[c] = load_stream16(kp + c * KSTEP);
 #pragma unroll
     for (int c = 0; c < Tl::NC; ++c) t.v[c] = load_stream16(vp + c * 256);
   };
@@ -124,6 +142,16 @@ decode_mfma_kernel(DecodeArgs a) {
     // S^T[token 4*grp+i][head col]
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (F8) {
+      if constexpr (KW) {
+        // lanes col >= 8 take chunk 2*grp of token col from load 1 (lane
+        // col - 8); lanes col < 8 take chunk 2*grp+1 from load 0 (col + 8)
+        const u32x4 a0 = t.k[0], a1 = t.k[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          t.k[0][j] = from_other_half<0xC>(a0[j], a1[j]);
+          t.k[1][j] = from_other_half<0x3>(a1[j], a0[j]);
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
         const uint32_t w0 = t.k[kk / 2][2 * (kk % 2)], w1 = t.k[kk / 2][2 * (kk % 2) + 1];
