@@ -440,6 +440,8 @@ def bench_prefill(args):
         f"Hkv={w.num_kv_heads} D={w.head_dim} dtype={w.dtype} "
         f"generated in {time.time()-t0:.1f}s")
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    fp8 = args.kv_dtype == "fp8"
+    cdt = torch.float8_e4m3fn if fp8 else tdt
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -448,7 +450,7 @@ def bench_prefill(args):
         return torch.from_numpy(a).cuda()
 
     kc, vc = pkv.new_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size,
-                              w.head_dim, tdt, fill=0.0)
+                              w.head_dim, cdt, fill=0.0)
     pkv.reshape_and_cache(dev(w.kv_k), dev(w.kv_v), kc, vc,
                           torch.from_numpy(w.context_slots()).cuda())
     ck, cv = dev(w.chunk_k()), dev(w.chunk_v())
@@ -501,8 +503,9 @@ def bench_prefill(args):
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     tok_s = T / (ms_step * 1e-3)
     cpu = None
+    tag = w.name + ("_fp8" if fp8 else "")
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_prefill(w, flops)
+        cpu = cpu_baseline_prefill(w, flops, fp8=fp8)
         cpu["gpu_speedup"] = round(flops / (ms_step * 1e-3) / 1e12 / cpu["value"], 1)
     rec = {"metric": "chunked-prefill attention TFLOP/s (causal, "
                      "4*head_dim flops per attended (token, head, key)) + "
@@ -511,9 +514,10 @@ def bench_prefill(args):
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": w.dtype, "data": "synthetic",
+           "dtype": f"{w.dtype}, e4m3 kv" if fp8 else w.dtype, "data": "synthetic",
            "config": {"workload": w.name, "num_seqs": w.num_seqs,
                       "query_tokens": T, "num_heads": w.num_heads,
+                      "kv_dtype": "e4m3" if fp8 else w.dtype,
                       "num_kv_heads": w.num_kv_heads,
                       "head_dim": w.head_dim, "block_size": w.block_size,
                       "num_blocks": w.num_blocks, "seed": args.seed,
@@ -530,7 +534,7 @@ def bench_prefill(args):
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                         "peak": peak, "unit": "TFLOP/s",
                         "frac": round(achieved / peak, 4),
-                        "traffic": stored_traffic("prefill_mfma_kernel", w.name),
+                        "traffic": stored_traffic("prefill_mfma_kernel", tag),
                         "kernel": "prefill_mfma_kernel",
                         "algorithmic_flops_per_launch": flops,
                         "mean_launch_ms": round(att_mean, 5)},
@@ -538,7 +542,7 @@ def bench_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline_prefill(w, flops_total, sample_rows=512):
+def cpu_baseline_prefill(w, flops_total, sample_rows=512, fp8=False):
     """The oracle on a bounded sample: every query head of `sample_rows`
     chunk tokens spread over the batch; flop rate scaled by the sampled
     tokens' share of the work."""
@@ -547,11 +551,17 @@ def cpu_baseline_prefill(w, flops_total, sample_rows=512):
     import oracle
 
     threads = oracle.default_threads()
+    cdt = "fp8" if fp8 else w.dtype
     kc, vc = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
-                             w.head_dim, w.dtype, fill="zero")
-    oracle.reshape_and_cache(w.kv_k, w.kv_v, kc, vc, w.kv_slots,
-                             w.num_kv_heads, w.head_dim, w.block_size,
-                             w.num_blocks, w.dtype)
+                             w.head_dim, cdt, fill="zero")
+    if fp8:
+        oracle.reshape_and_cache_fp8(w.kv_k, w.kv_v, kc, vc, w.kv_slots,
+                                     w.num_kv_heads, w.head_dim, w.block_size,
+                                     w.num_blocks, w.dtype, 1.0, 1.0)
+    else:
+        oracle.reshape_and_cache(w.kv_k, w.kv_v, kc, vc, w.kv_slots,
+                                 w.num_kv_heads, w.head_dim, w.block_size,
+                                 w.num_blocks, w.dtype)
     T = w.q.shape[0]
     rows = np.linspace(0, T - 1, sample_rows).astype(np.int64)
     sel = np.stack([np.repeat(rows, w.num_heads),
@@ -564,7 +574,8 @@ def cpu_baseline_prefill(w, flops_total, sample_rows=512):
     t1 = time.perf_counter()
     out = oracle.paged_prefill(w.q, kc, vc, w.block_tables, w.context_lens,
                                qsl, w.scale, w.block_size, w.num_kv_heads,
-                               w.num_blocks, w.dtype, sel=sel, threads=threads)
+                               w.num_blocks, w.dtype, sel=sel, threads=threads,
+                               cache_dtype=cdt)
     dt = time.perf_counter() - t1
     assert np.all(np.isfinite(out))
     log(f"[bench] oracle sample {dt:.2f}s")

@@ -266,7 +266,8 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
                                const pkv_dims *dims, pkv_stream_t stream);
 
 /* Chunked prefill over 8-bit caches (same rows and causality as
- * paged_attention_prefill), on the vector kernel for every dims->dtype. */
+ * paged_attention_prefill).  fp16 and bf16 run on the matrix cores, the
+ * codes widened exactly to dims->dtype; fp32 runs on the vector ALUs. */
 int paged_attention_prefill_fp8(void *out, const void *q, const void *k_cache,
                                 const void *v_cache, const int32_t *block_tables,
                                 const int32_t *context_lens,

@@ -236,9 +236,9 @@ int prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
   if (rc != PKV_OK) return rc;
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
   if (num_query_tokens < 0 || max_query_len < 0) return PKV_ERR_SHAPE;
-  // fp16/bf16 queries over 16-bit caches run on the matrix cores; fp32 and
-  // 8-bit caches on the vector kernel, one workgroup per (query row, head)
-  const bool on_mfma = dims->dtype != PKV_F32 && cache_dtype == kCacheSame;
+  // fp16/bf16 queries run on the matrix cores (16-bit or 8-bit caches);
+  // fp32 on the vector kernel, one workgroup per (query row, head)
+  const bool on_mfma = dims->dtype != PKV_F32;
   if (!on_mfma && (int64_t)num_query_tokens * dims->num_heads > INT_MAX) return PKV_ERR_SHAPE;
   const int G = dims->num_heads / dims->num_kv_heads;
   const u128 qb = (u128)num_query_tokens * (u128)dims->num_heads * (u128)dims->head_dim *

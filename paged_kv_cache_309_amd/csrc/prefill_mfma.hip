@@ -1,5 +1,5 @@
 // prefill_mfma.hip - multi-query paged attention for chunked prefill on the
-// matrix cores (fp16 / bf16).
+// matrix cores (fp16 / bf16 queries; caches of the query's type or E4M3).
 //
 // A long prompt is processed in chunks that share iterations with ongoing
 // decodes ("Inside vLLM: How PagedAttention Eliminates KV-Cache Memory
@@ -44,6 +44,14 @@
 // latest rows (longest prefixes) first, so the sequence's K/V stay in that
 // XCD's L2 while its row blocks run.
 //
+// 8-bit caches: the ring holds the 1-byte codes (half the bytes per stage).
+// A 16-byte K read gives 16 dims of one token, widened exactly to the
+// 16-bit type of q with one packed conversion per pair of codes, and feeds
+// two logit products; q is loaded in the matching dimension order.  For V,
+// one 16-byte read per tile gives the four tokens of four consecutive dims,
+// so n-tile 4u + j takes dim 64u + 4m + j.  The key scale is folded into the
+// logit scale, the value scale into the final normalisation.
+//
 // Probabilities enter the value product rounded to the 16-bit type of q
 // (nearest even, one packed conversion per pair).  The running sum of each
 // row comes out of one more 16x16x32 product with an A operand of ones, so
@@ -70,22 +78,27 @@ int64_t prefill_grid(int num_seqs, int num_kv_heads, int q_blocks) {
 }
 
 // LDS ring of super-tiles.  One super-tile is four 16-token pieces: K of
-// tile 0, K of tile 1, V of tile 0, V of tile 1, each 16 * D * 2 bytes and
-// each filled by one wavefront with direct global-to-LDS loads (64 lanes x
-// 16 bytes per instruction, lane i writing bytes 16i .. 16i+15 of its
-// 1 KiB block).  V pieces keep the HBM layout.  K pieces are stored with
-// the 16-byte chunks of each token row permuted: physical chunk p of row r
-// holds logical chunk p ^ (r % CR) (CR = chunks per row), so that the 16
-// lanes reading the same logical chunk of 16 different rows hit different
-// LDS banks.  The permutation is applied through the global address each
-// lane loads from.
-template <int D>
+// tile 0, K of tile 1, V of tile 0, V of tile 1, each 16 * D * E bytes (E:
+// cache element bytes) and each filled by one wavefront with direct
+// global-to-LDS loads (64 lanes x 16 bytes per instruction, lane i writing
+// bytes 16i .. 16i+15 of its 1 KiB block).  V pieces keep the HBM layout.
+// K pieces are stored with the 16-byte chunks of each token row permuted:
+// physical chunk p of row r holds logical chunk p ^ key(r), so that the 16
+// lanes reading the same logical chunk of 16 different rows (one pass of a
+// 16-byte LDS read) hit 16 different 16-byte bank groups of the 256-byte
+// bank line.  key(r) = (r / RPL) % CR, with CR chunks per row and RPL rows
+// per bank line.  The permutation is applied through the global address
+// each lane loads from.
+template <int CT, int D>
 struct PrefillRing {
-  static constexpr int PIECE = 16 * D * 2;
+  static constexpr int ROWB = D * Elem<CT>::bytes;  // bytes per K row
+  static constexpr int PIECE = 16 * ROWB;
   static constexpr int TILE = 4 * PIECE;
   static constexpr int STAGES = 4;
-  static constexpr int CR = 2 * D / 16;  // 16-byte chunks per K row
+  static constexpr int CR = ROWB / 16;  // 16-byte chunks per K row
+  static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;
   static constexpr int LOADS = PIECE / 1024;  // per wavefront and super-tile
+  __device__ static __forceinline__ int key(int r) { return (r / RPL) % CR; }
 };
 
 __device__ __forceinline__ u32x4 lds16(const char *p) {
@@ -112,14 +125,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
 }
 
-template <int QT, int D, int BS>
+// QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
+template <int QT, int CT, int D, int BS>
 __global__ void __launch_bounds__(kPrefillThreads)
 prefill_mfma_kernel(PrefillArgs a) {
   using Ops = MfmaOps<QT>;
-  using RG = PrefillRing<D>;
+  using RG = PrefillRing<CT, D>;
+  constexpr bool F8 = CT == DT_FP8;
+  constexpr int E = Elem<CT>::bytes;
   constexpr int KC = D / 32;   // logit MFMAs per 16-token tile and row tile
-  constexpr int NC = D / 32;   // 16-byte V reads per lane and tile
+  constexpr int NC = D / 32;   // 16-byte V reads per lane and tile (16-bit)
   constexpr int NT = D / 16;   // value n-tiles
+  constexpr int V8 = D / 64;   // 16-byte V reads per lane and tile (8-bit)
   constexpr int NQ = kPrefillNQ;
   constexpr int S = RG::STAGES;
   __shared__ __attribute__((aligned(1024))) char ring[S * RG::TILE];
@@ -168,10 +185,14 @@ prefill_mfma_kernel(PrefillArgs a) {
     pos[qt] = valid ? L - C + j : -1;
     orow[qt] = ((size_t)(q0 + j) * Hq + g * G + hh) * D;
     const char *qp = static_cast<const char *>(a.q) + orow[qt] * 2;
+    // the eight dims logit product kk takes from this lane: chunk kk*4+grp
+    // of the row (16-bit caches); half kk%2 of the 16 dims of 8-bit chunk
+    // (kk/2)*4+grp
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk)
-      qop[qt][kk] = valid ? *reinterpret_cast<const u32x4 *>(qp + (kk * 4 + grp) * 16)
-                          : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < KC; ++kk) {
+      const int off = F8 ? 32 * ((kk / 2) * 4 + grp) + 16 * (kk % 2) : (kk * 4 + grp) * 16;
+      qop[qt][kk] = valid ? *reinterpret_cast<const u32x4 *>(qp + off) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   // the queries are in registers before the ring's loads are counted
   wait_vm<0>();
@@ -180,17 +201,17 @@ prefill_mfma_kernel(PrefillArgs a) {
   const __attribute__((address_space(4))) int32_t *trow =
       (const __attribute__((address_space(4))) int32_t *)(a.block_tables +
                                                           (size_t)s * a.max_blocks);
-  const size_t block_bytes = (size_t)Hkv * BS * D * 2;
+  const size_t block_bytes = (size_t)Hkv * BS * D * E;
   const char *src_base = static_cast<const char *>(w < 2 ? a.k_cache : a.v_cache) +
-                         (size_t)g * BS * D * 2;
+                         (size_t)g * BS * D * E;
   // this lane's source offset inside the piece, per 1 KiB block b
   uint32_t lane_off[RG::LOADS];
 #pragma unroll
   for (int b = 0; b < RG::LOADS; ++b) {
     if (w < 2) {
-      const int rows_per_kib = 1024 / (2 * D);
+      const int rows_per_kib = 1024 / RG::ROWB;
       const int r = b * rows_per_kib + lane / RG::CR, p = lane % RG::CR;
-      lane_off[b] = (uint32_t)(r * 2 * D + ((p ^ (r % RG::CR)) * 16));
+      lane_off[b] = (uint32_t)(r * RG::ROWB + ((p ^ RG::key(r)) * 16));
     } else {
       lane_off[b] = (uint32_t)(b * 1024 + lane * 16);
     }
@@ -208,7 +229,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     // phys is in [0, num_blocks) and a block is far below 4 GiB: an unsigned
     // 32 x 32 -> 64-bit product
     const char *src = src_base + (uint64_t)(unsigned)phys * (unsigned)block_bytes +
-                      (tb % BS) * D * 2;
+                      (tb % BS) * D * E;
     char *dst = ring + stage * RG::TILE + w * RG::PIECE;
 #pragma unroll
     for (int b = 0; b < RG::LOADS; ++b)
@@ -236,26 +257,55 @@ prefill_mfma_kernel(PrefillArgs a) {
     // K operands of both tiles first: the logit products wait only for them,
     // and the value reads complete while those products run
     u32x4 kop[2][KC];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const int c = kk * 4 + grp;
-        kop[st][kk] = lds16(base + st * RG::PIECE + col * 2 * D + ((c ^ (col % RG::CR)) * 16));
-      }
-    // value operand of n-tile 2u+j: dim 32u + 2*col + j, four tokens of tile
-    // 0 then the same four of tile 1 (8 bytes each, one piece apart, so one
-    // two-address LDS read fills the operand's registers in place)
     u32x4 va[NT];
+    u32x4 vraw[F8 ? V8 : 1][2];
+    if constexpr (F8) {
+      u32x4 kraw[2][KC / 2];
 #pragma unroll
-    for (int u = 0; u < NC; ++u)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const char *v0 = base + 2 * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8 + 8 * j;
-        const u32x2 lo = *(const volatile __attribute__((address_space(3))) u32x2 *)v0;
-        const u32x2 hi = *(const volatile __attribute__((address_space(3))) u32x2 *)(v0 + RG::PIECE);
-        va[2 * u + j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        for (int k2 = 0; k2 < KC / 2; ++k2) {
+          const int c = k2 * 4 + grp;
+          kraw[st][k2] = lds16(base + st * RG::PIECE + col * RG::ROWB + ((c ^ RG::key(col)) * 16));
+        }
+      // four tokens of dims 64u + 4*col .. +3, tile 0 and tile 1
+#pragma unroll
+      for (int u = 0; u < V8; ++u) {
+        const char *v0 = base + 2 * RG::PIECE + (grp * D + 64 * u + 4 * col) * 4;
+        vraw[u][0] = lds16(v0);
+        vraw[u][1] = lds16(v0 + RG::PIECE);
       }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int k2 = 0; k2 < KC / 2; ++k2)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t w0 = kraw[st][k2][2 * h], w1 = kraw[st][k2][2 * h + 1];
+            kop[st][2 * k2 + h] = u32x4{fp8x2_to_16<QT>(w0, false), fp8x2_to_16<QT>(w0, true),
+                                        fp8x2_to_16<QT>(w1, false), fp8x2_to_16<QT>(w1, true)};
+          }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          const int c = kk * 4 + grp;
+          kop[st][kk] = lds16(base + st * RG::PIECE + col * RG::ROWB + ((c ^ RG::key(col)) * 16));
+        }
+      // value operand of n-tile 2u+j: dim 32u + 2*col + j, four tokens of
+      // tile 0 then the same four of tile 1 (8 bytes each, one piece apart,
+      // so one two-address LDS read fills the operand's registers in place)
+#pragma unroll
+      for (int u = 0; u < NC; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const char *v0 = base + 2 * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8 + 8 * j;
+          const u32x2 lo = *(const volatile __attribute__((address_space(3))) u32x2 *)v0;
+          const u32x2 hi = *(const volatile __attribute__((address_space(3))) u32x2 *)(v0 + RG::PIECE);
+          va[2 * u + j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    }
     // logits of both row tiles first, so that one tile's softmax can run on
     // the vector ALUs while the other's products are still in the matrix
     // cores
@@ -286,14 +336,34 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int nvalid = max(0, min(4, L - (32 * n + 16 * st + 4 * grp)));
-        const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-        const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+        if constexpr (F8) {
+          const uint32_t mk = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          va[t][2 * st] &= m01;
-          va[t][2 * st + 1] &= m23;
+          for (int u = 0; u < V8; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vraw[u][st][j] &= mk;
+        } else {
+          const uint32_t m01 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+          const uint32_t m23 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            va[t][2 * st] &= m01;
+            va[t][2 * st + 1] &= m23;
+          }
         }
       }
+    }
+    if constexpr (F8) {
+      // n-tile 4u + j: dim 64u + 4*col + j, its four tokens of tile 0 then
+      // of tile 1
+#pragma unroll
+      for (int u = 0; u < V8; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = vraw[u][0][j], w1 = vraw[u][1][j];
+          va[4 * u + j] = u32x4{fp8x2_to_16<QT>(w0, false), fp8x2_to_16<QT>(w0, true),
+                                fp8x2_to_16<QT>(w1, false), fp8x2_to_16<QT>(w1, true)};
+        }
     }
     // running maxima (base-2 units), moved only when a logit exceeds one by
     // more than the slack somewhere in the wave: one test for all row tiles
@@ -385,51 +455,70 @@ prefill_mfma_kernel(PrefillArgs a) {
   }
   static_assert(S == 4, "the general loop's waits cover S - 2 = 2 later super-tiles");
 
-  // normalise and store: n-tile 2u+j, row m = 4*grp + i is dim 32u + 2m + j
-  // of the lane's query row; the two n-tiles of a chunk give two adjacent
-  // dims, stored as one 32-bit word
+  // normalise and store: row m = 4*grp + i of n-tile 2u+j is dim
+  // 32u + 2m + j of the lane's query row (16-bit caches; two adjacent dims
+  // stored as one 32-bit word), of n-tile 4u+j dim 64u + 4m + j (8-bit
+  // caches; four adjacent dims stored as one 64-bit word)
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const float lt = lsum[qt][0];
     if (row0 + qt * 16 + col > row_last) continue;  // no row in this column
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     uint32_t *op = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + orow[qt]);
+    if constexpr (F8) {
 #pragma unroll
-    for (int u = 0; u < NC; ++u) {
+      for (int u = 0; u < V8; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * u + 2 * (4 * grp + i);
-        op[d >> 1] = from_f32<QT>(acc[qt][2 * u][i] * inv) |
-                     (from_f32<QT>(acc[qt][2 * u + 1][i] * inv) << 16);
+        for (int i = 0; i < 4; ++i) {
+          const int d = 64 * u + 4 * (4 * grp + i);
+          const u32x2 wv = {from_f32<QT>(acc[qt][4 * u][i] * inv) |
+                                (from_f32<QT>(acc[qt][4 * u + 1][i] * inv) << 16),
+                            from_f32<QT>(acc[qt][4 * u + 2][i] * inv) |
+                                (from_f32<QT>(acc[qt][4 * u + 3][i] * inv) << 16)};
+          *reinterpret_cast<u32x2 *>(op + (d >> 1)) = wv;
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * u + 2 * (4 * grp + i);
+          op[d >> 1] = from_f32<QT>(acc[qt][2 * u][i] * inv) |
+                       (from_f32<QT>(acc[qt][2 * u + 1][i] * inv) << 16);
+        }
       }
     }
   }
 }
 
-template <int QT, int D, int BS>
+template <int QT, int CT, int D, int BS>
 static hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
   const int64_t n = prefill_grid(a.num_seqs, a.num_kv_heads, a.q_blocks);
-  hipLaunchKernelGGL((prefill_mfma_kernel<QT, D, BS>), dim3((unsigned)n), dim3(kPrefillThreads),
-                     0, st, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS>), dim3((unsigned)n),
+                     dim3(kPrefillThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int QT>
+template <int QT, int CT>
 static hipError_t launch_prefill_dt(const PrefillArgs &a, int head_dim, int block_size,
                                     hipStream_t st) {
   if (head_dim == 128)
-    return block_size == 16 ? launch_prefill<QT, 128, 16>(a, st)
-                            : launch_prefill<QT, 128, 32>(a, st);
-  return block_size == 16 ? launch_prefill<QT, 64, 16>(a, st) : launch_prefill<QT, 64, 32>(a, st);
+    return block_size == 16 ? launch_prefill<QT, CT, 128, 16>(a, st)
+                            : launch_prefill<QT, CT, 128, 32>(a, st);
+  return block_size == 16 ? launch_prefill<QT, CT, 64, 16>(a, st)
+                          : launch_prefill<QT, CT, 64, 32>(a, st);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int dtype, int cache_dtype, int head_dim,
                                int block_size, int max_query_len, hipStream_t st) {
-  (void)cache_dtype;
   (void)max_query_len;
   if (a.num_seqs == 0 || a.q_blocks == 0) return hipSuccess;
-  if (dtype == DT_F16) return launch_prefill_dt<DT_F16>(a, head_dim, block_size, st);
-  return launch_prefill_dt<DT_BF16>(a, head_dim, block_size, st);
+  if (cache_dtype == DT_FP8) {
+    if (dtype == DT_F16) return launch_prefill_dt<DT_F16, DT_FP8>(a, head_dim, block_size, st);
+    return launch_prefill_dt<DT_BF16, DT_FP8>(a, head_dim, block_size, st);
+  }
+  if (dtype == DT_F16) return launch_prefill_dt<DT_F16, DT_F16>(a, head_dim, block_size, st);
+  return launch_prefill_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, st);
 }
 
 }  // namespace pkv
