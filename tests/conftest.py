@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # a GPU test never runs silently on a machine without a GPU: it is
-    # skipped there, and fails loudly on a GPU box whose library is missing
+    # skipped there, and fails loudly on a GPU machine whose library is missing
     try:
         import torch
         have_gpu = torch.cuda.is_available()
