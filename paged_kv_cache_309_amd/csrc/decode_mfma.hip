@@ -69,11 +69,11 @@ decode_mfma_kernel(DecodeArgs a) {
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
 
-  // LDS: the merge of the 4 wavefronts; before the loop it holds the sort
-  // keys of the longest-first order
+  // LDS: the merge of the 4 wavefronts; before the loop it holds the length
+  // histogram of the longest-first order
   __shared__ float sm_o[kDecodeWaves][16][D + 4];
   __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
-  static_assert(sizeof(sm_o) >= kOrderMaxSeqs * sizeof(int), "order scratch");
+  static_assert(sizeof(sm_o) >= kOrderScratchInts * sizeof(int), "order scratch");
   const int s = SPLIT ? (int)blockIdx.y
                       : longest_first_seq<kDecodeThreads>(
                             a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,

@@ -84,10 +84,10 @@ decode_vector_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
 
   // LDS: the final merge of partial states; before the loop it holds the
-  // sort keys of the longest-first order
+  // length histogram of the longest-first order
   __shared__ float sm_acc[16][D];
   __shared__ float sm_m[16], sm_l[16];
-  static_assert(sizeof(sm_acc) >= kOrderMaxSeqs * sizeof(int), "order scratch");
+  static_assert(sizeof(sm_acc) >= kOrderScratchInts * sizeof(int), "order scratch");
   const int s = MQ ? seq_of_row(a.query_start_loc, a.num_seqs, qrow)
                : SPLIT ? (int)blockIdx.y
                        : longest_first_seq<kDecodeThreads>(

@@ -149,40 +149,78 @@ __device__ __forceinline__ bool wave_any(bool pred) {
 // differ in length by up to two orders of magnitude; the dispatcher starts
 // workgroups in grid order, so a long sequence that starts late stretches
 // the end of the kernel.  Workgroup row r therefore processes the sequence
-// of rank r in decreasing context length (ties in sequence order), computed
-// in every workgroup from context_lens: each thread owns up to
-// kOrderMaxSeqs / blockDim candidates and counts the keys larger than its
-// candidate's.  Keys pack (length, sequence) into one int:
-// (L << 10) | (1023 - s), unique, and larger for longer (then earlier)
-// sequences.  Above kOrderMaxSeqs sequences, or lengths of 2^21 tokens or
-// more, the grid order is kept.  `keys` is LDS scratch of kOrderMaxSeqs
-// ints; the result only chooses which workgroup does which sequence, never
-// the arithmetic.
-constexpr int kOrderMaxSeqs = 1024;
+// of rank r in an order of decreasing context length, computed in every
+// workgroup from context_lens with a counting select:
+//   * lengths (clamped to [0, max_tokens]) fall into 256 buckets of equal
+//     width 2^sh, bucket (max_tokens - L) >> sh, so bucket 0 holds the
+//     longest;
+//   * a histogram of the buckets in LDS and its prefix sum give the bucket
+//     that holds rank r and r's place k inside it;
+//   * the k-th sequence of that bucket in sequence order is the result.
+// The order is longest-first up to the bucket width (max_tokens / 256
+// tokens or less).  Each thread does O(S / 256 + 1) work.  `scratch` is LDS
+// of at least kOrderScratchInts ints, free for reuse once this returns; the
+// result only chooses which workgroup does which sequence, never the
+// arithmetic.
+constexpr int kOrderBuckets = 256;
+constexpr int kOrderScratchInts = kOrderBuckets + 8;
 
 template <int NT>
 __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, int S,
-                                                 int max_tokens, int r, int *keys) {
-  if (S > kOrderMaxSeqs || max_tokens >= (1 << 21)) return r;
-  __shared__ int chosen;
-  const int tid = threadIdx.x;
-  const int Sp = (S + 3) & ~3;
-  for (int i = tid; i < Sp; i += NT) {
-    int L = i < S ? context_lens[i] : -1;
-    L = min(L, max_tokens);
-    keys[i] = i < S ? ((max(L, 0) << 10) | (1023 - i)) : -1;  // padding: smallest
+                                                 int max_tokens, int r, int *scratch) {
+  static_assert(NT == kOrderBuckets, "one thread per bucket");
+  __shared__ int sel_bucket, sel_k, chosen;
+  int *hist = scratch;                  // kOrderBuckets counters
+  int *wsum = scratch + kOrderBuckets;  // one total per wavefront
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  max_tokens = max(max_tokens, 0);
+  int sh = 0;
+  while ((max_tokens >> sh) >= kOrderBuckets) ++sh;
+  auto bucket = [&](int i) {
+    const int L = max(0, min(context_lens[i], max_tokens));
+    return (max_tokens - L) >> sh;
+  };
+  hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < S; i += NT) atomicAdd(&hist[bucket(i)], 1);
+  __syncthreads();
+  // inclusive prefix sum of the histogram: within each wavefront, then the
+  // totals of the wavefronts before it
+  const int h = hist[tid];
+  int x = h;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) x += wsum[q];
+  if (x - h <= r && r < x) {  // exactly one bucket holds rank r (r < S)
+    sel_bucket = tid;
+    sel_k = r - (x - h);
   }
   __syncthreads();
-  for (int i = tid; i < S; i += NT) {
-    const int key = keys[i];
-    int rank = 0;
-    for (int j = 0; j < Sp; j += 4) {
-      const int4 k4 = *reinterpret_cast<const int4 *>(&keys[j]);
-      rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
+  const int bsel = sel_bucket, k = sel_k;
+  // the k-th member of bucket bsel in sequence order, NT sequences a pass
+  int base = 0;
+  for (int c = 0; c < S; c += NT) {
+    const int i = c + tid;
+    const bool f = i < S && bucket(i) == bsel;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(f);
+    const int before_lane = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+    __syncthreads();
+    int before = base, total = 0;
+    for (int q = 0; q < NT / 64; ++q) {
+      if (q < w) before += wsum[q];
+      total += wsum[q];
     }
-    if (rank == r) chosen = i;
+    if (f && before + before_lane == k) chosen = i;
+    base += total;
+    __syncthreads();  // wsum is rewritten by the next pass
+    if (base > k) break;  // uniform: every thread holds the same base
   }
-  __syncthreads();
   return chosen;
 }
 

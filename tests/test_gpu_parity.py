@@ -245,8 +245,8 @@ def test_edge_contexts(dtype):
 @pytest.mark.parametrize("S,Hq,Hkv,dtype", [(1024, 2, 2, "f16"), (1025, 2, 2, "bf16"),
                                             (1500, 8, 2, "bf16"), (1300, 4, 4, "f32")])
 def test_many_sequences(S, Hq, Hkv, dtype):
-    """More sequences than the in-workgroup longest-first order handles
-    (1024): the grid order is kept, the result is the same."""
+    """Batches of 1024 to 1500 sequences: the longest-first order's counting
+    select makes several passes over the sequences; the result is the same."""
     w = wl.random_case(9000 + S, num_seqs=S, max_len=60, num_heads=Hq,
                        num_kv_heads=Hkv, head_dim=64, block_size=16, dtype=dtype,
                        pool_factor=1.3)
@@ -260,9 +260,10 @@ def test_many_sequences(S, Hq, Hkv, dtype):
         compare(got, want, dtype, f"S={S} {variant}")
 
 
-def test_table_wider_than_the_order_key():
+def test_very_wide_block_table():
     """A block table of 2^17 entries (2^21 tokens at 16 per block): the
-    longest-first keys would overflow, so the grid order is kept."""
+    longest-first order's length buckets are 2^13 tokens wide, so every
+    sequence falls in one bucket; the result is the same."""
     w = wl.random_case(9100, num_seqs=3, max_len=90, num_heads=4, num_kv_heads=2,
                        head_dim=64, block_size=16, dtype="bf16", pool_factor=1.5)
     MB = 1 << 17
@@ -275,3 +276,36 @@ def test_table_wider_than_the_order_key():
     dev = Dev(w)
     kd, vd = dev.cache_from_host(kc, vc)
     compare(to_f64(dev.decode(kd, vd)), want, "bf16", "wide table")
+
+
+@pytest.mark.parametrize("S", [1, 255, 256, 257, 1024, 4097])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
+def test_longest_first_order_covers_every_sequence(S, Hq, Hkv):
+    """Single-pass launches map workgroup row r to the sequence of rank r in
+    decreasing length.  With one output row per sequence pre-filled with NaN,
+    every sequence must be computed exactly as the oracle computes it: a
+    mapping that skipped or repeated a sequence leaves NaN or a wrong row.
+    Lengths mix long runs of ties (half the batch shares one length) with a
+    spread from 0 to 200 tokens, on the vector (MHA) and the matrix-core
+    (GQA) kernel."""
+    import paged_kv_cache_309_amd as pkv
+    rng = np.random.default_rng(9400 + S + Hq)
+    lens = rng.integers(0, 200, size=S, endpoint=True)
+    lens[rng.random(S) < 0.5] = 77
+    w = wl.build(f"order{S}", lens=lens, num_heads=Hq, num_kv_heads=Hkv, head_dim=64,
+                 block_size=16, dtype="bf16", seed=9400 + S + Hq, pool_factor=1.2,
+                 max_blocks_per_seq=13, rng=rng)
+    print(f"[order] S={S} Hq={Hq} Hkv={Hkv} ties at 77: {int((lens == 77).sum())}",
+          flush=True)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    q = to_torch(w.q, "bf16")
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, kd, vd, torch.from_numpy(w.block_tables).cuda(),
+                               torch.from_numpy(w.context_lens).cuda(), w.scale)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    compare(got, want, "bf16", f"order S={S}")
