@@ -295,11 +295,12 @@ decode_mfma_kernel(DecodeArgs a) {
     const int h = g * G + hh;
     num *= a.v_scale;  // value dequantisation (1 for 16-bit caches)
     if constexpr (SPLIT) {
+      // partials written through L2 (nothing in this kernel reads them)
       const size_t pi = ((size_t)s * Hq + h) * a.num_parts + part;
-      a.ws_o[pi * D + d] = num;
+      store_through(&a.ws_o[pi * D + d], num);
       if (d == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = den;
+        store_through(&a.ws_m[pi], M);
+        store_through(&a.ws_l[pi], den);
       }
     } else {
       store_elem<QT>(a.out, ((size_t)s * Hq + h) * D + d, num / den);

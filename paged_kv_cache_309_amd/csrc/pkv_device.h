@@ -94,6 +94,15 @@ __device__ __forceinline__ void store_elem(void *base, size_t idx, float x) {
   }
 }
 
+// A store that writes through L2 to memory (a relaxed store at system
+// scope).  Lines a kernel leaves dirty in L2 are written back when it ends,
+// and that write-back runs far below the HBM write rate; results that no
+// later read in the same kernel wants go through instead.  Used where a
+// wave's store instruction covers whole 128-byte lines.
+__device__ __forceinline__ void store_through(float *p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // DPP lane permutations inside a row of 16 lanes.
 enum : int {
   DPP_QUAD_XOR1 = 0xB1,    // quad_perm [1,0,3,2]

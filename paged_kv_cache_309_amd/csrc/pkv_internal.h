@@ -13,6 +13,8 @@ enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 // Threads per workgroup of the decode kernels: four wave64 wavefronts.
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = 4;
+// Most partitions one wave of the vector kernel's split launch computes.
+constexpr int kMaxPartsPerWave = 4;
 
 struct DecodeArgs {
   void *out;              // [S, Hq, D] storage type (single pass, reduce)
@@ -34,6 +36,8 @@ struct DecodeArgs {
   int block_size;
   int part_tokens;        // tokens per partition (split); unused otherwise
   int num_parts;          // partitions per sequence (1 for single pass)
+  int parts_per_wave = 1; // split on the vector kernel: consecutive partitions
+                          // one wave computes (1 .. kMaxPartsPerWave)
   // multi-query (chunked prefill) on the vector kernel: q / out hold
   // num_query_tokens rows; sequence s's rows are query_start_loc[s] ..
   // query_start_loc[s+1]-1, the last tokens of its context (causal).

@@ -157,3 +157,13 @@ def host_bits(a: np.ndarray) -> np.ndarray:
     if a.dtype.itemsize == 1:
         return a.view(np.uint8)
     return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)
+
+
+def split_parts_per_wave(num_seqs: int, num_heads: int, num_parts: int) -> int:
+    """Partitions one wave of the vector kernel's split launch computes, by
+    the launcher's rule: enough for every wave of the grid to be resident
+    (16 waves per compute unit), at most 4, and at most a quarter of the
+    partitions so that each of a workgroup's four waves gets some."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ppw = -(-num_seqs * num_heads * num_parts // (cus * 16))
+    return max(1, min(ppw, max(1, num_parts // 4), 4))

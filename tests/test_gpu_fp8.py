@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import compare, to_f64, to_torch, TORCH
+from gpu_util import compare, split_parts_per_wave, to_f64, to_torch, TORCH
 
 pytestmark = pytest.mark.gpu
 FP8 = torch.float8_e4m3fn
@@ -222,3 +222,30 @@ def test_full_size_workloads(name):
     for variant in ("single", "split"):
         out = to_f64(decode(w, kd, vd, variant, 512, ks, vs))
         compare(out[sel[:, 0], sel[:, 1]], want, w.dtype, f"{name} {variant}")
+
+
+def test_split_several_partitions_per_wave():
+    """E4M3 caches on the vector kernel's split walk with one wave carried
+    through four consecutive partitions (rows 2 and 3 park nothing: a row
+    of 8-bit values holds 64 dims)."""
+    ks, vs = 0.25, 2.0
+    w = wl.random_case(7900, num_seqs=64, max_len=600, num_heads=8,
+                       num_kv_heads=8, head_dim=128, block_size=16,
+                       dtype="bf16", pool_factor=1.3)
+    part = 16
+    P = -(-(w.max_blocks_per_seq * w.block_size) // part)
+    ppw = split_parts_per_wave(w.num_seqs, w.num_heads, P)
+    print(f"[fp8 split ppw] P={P} parts/wave={ppw}", flush=True)
+    if ppw < 2:
+        pytest.skip("this device holds the whole grid at one partition per wave")
+    kc0, vc0 = oracle.new_pool(w.num_blocks, w.num_kv_heads, w.block_size,
+                               w.head_dim, "fp8")
+    kc, vc = oracle_write(w, ks, vs, kc0, vc0)
+    want = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.context_lens,
+                               w.scale, w.block_size, w.num_kv_heads,
+                               w.num_blocks, w.dtype, cache_dtype="fp8",
+                               k_scale=ks, v_scale=vs)
+    kd, vd = fp8_pool_to_dev(kc, vc, w.num_blocks, w.num_kv_heads,
+                             w.block_size, w.head_dim)
+    got = to_f64(decode(w, kd, vd, "split", part, ks, vs))
+    compare(got, want, w.dtype, f"fp8 split{part} parts/wave={ppw}")

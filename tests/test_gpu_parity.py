@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as wl
 from gpu_util import (Dev, compare, host_bits, oracle_out, oracle_pool,
-                      pool_bits, to_f64, to_torch)
+                      pool_bits, split_parts_per_wave, to_f64, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -309,3 +309,37 @@ def test_longest_first_order_covers_every_sequence(S, Hq, Hkv):
     got = to_f64(out)
     assert np.all(np.isfinite(got))
     compare(got, want, "bf16", f"order S={S}")
+
+
+SPLIT_MULTI = [
+    # dtype, bs, heads (MHA), D, S, max_len, partition: grids large enough
+    # that one wave computes 2, 3 or 4 consecutive partitions
+    ("f16", 16, 8, 64, 64, 600, 16),
+    ("bf16", 32, 4, 128, 64, 1000, 32),
+    ("f32", 16, 4, 128, 160, 800, 48),
+    ("bf16", 16, 16, 128, 48, 2000, 64),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SPLIT_MULTI)))
+def test_split_several_partitions_per_wave(i):
+    """The vector kernel's split walk carries one wave through consecutive
+    partitions, parking each partial state at the partition's last tile and
+    starting afresh; ragged lengths end walks inside a partition, and
+    zero-length sequences have none.  Every output matches the oracle."""
+    dtype, bs, H, D, S, max_len, part = SPLIT_MULTI[i]
+    w = wl.random_case(9300 + i, num_seqs=S, max_len=max_len, num_heads=H,
+                       num_kv_heads=H, head_dim=D, block_size=bs, dtype=dtype,
+                       pool_factor=1.3)
+    P = -(-(w.max_blocks_per_seq * bs) // part)
+    ppw = split_parts_per_wave(S, H, P)
+    print(f"[split ppw] case {i} {dtype} bs={bs} H={H} D={D} S={S} "
+          f"P={P} parts/wave={ppw}", flush=True)
+    if ppw < 2:
+        pytest.skip("this device holds the whole grid at one partition per wave")
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    got = to_f64(dev.decode(kd, vd, "split", part))
+    compare(got, want, dtype, f"split{part} parts/wave={ppw}")
