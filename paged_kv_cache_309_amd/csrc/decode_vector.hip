@@ -381,8 +381,10 @@ static hipError_t launch_vec(const DecodeArgs &a, bool split, hipStream_t st) {
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
+        cus <= 0) {
+      (void)hipGetLastError();  // a failed query must not read as a failed launch
       cus = 256;
+    }
     const int64_t units = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
     const int64_t resident = (int64_t)cus * 4 * kDecodeWaves;
     int64_t ppw = (units + resident - 1) / resident;
