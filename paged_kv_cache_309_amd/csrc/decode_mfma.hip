@@ -11,8 +11,12 @@
 // vector kernel ("Paged Attention" placement notes, section "Paged
 // Attention's Approach").
 //
-// One workgroup (4 wavefronts) per (sequence, KV head[, partition]); each
-// K/V tile is read from HBM once for all G heads.  Per 16-token tile a
+// One workgroup (4 wavefronts) per (sequence, KV head); each K/V tile is
+// read from HBM once for all G heads.  Split launches give each wavefront a
+// partition of its own instead (wave w of workgroup z: partition 4z + w),
+// walked as one stream of tiles.  The wave's state is already the whole
+// partial of its G heads, so it goes to the workspace through the wave's
+// own slice of LDS, with no barrier and no merge across wavefronts.  Per 16-token tile a
 // wavefront issues D/32 v_mfma_f32_16x16x32 for the logits (keys as the A
 // operand: 16 tokens x 32 dims, one token per lane-column; queries as B, one
 // head per column) and 2 x D/16 v_mfma_f32_16x16x16 for the values (values
@@ -64,7 +68,7 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int NT = D / 16;          // value n-tiles
   constexpr bool KW = F8 && D == 128; // K loaded as whole rows, then exchanged
 
-  const int g = blockIdx.x, part = blockIdx.z;
+  const int g = blockIdx.x;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
@@ -80,6 +84,10 @@ decode_mfma_kernel(DecodeArgs a) {
                             reinterpret_cast<int *>(&sm_o[0][0][0]));
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  // split: this wave's partition (the split path has no workgroup barrier,
+  // so a wave with nothing to do leaves at once)
+  const int part = SPLIT ? (int)blockIdx.z * kDecodeWaves + w : 0;
+  if (SPLIT && part >= a.num_parts) return;
 
   int L = a.context_lens[s];
   L = max(0, min(L, a.max_blocks * BS));
@@ -115,7 +123,12 @@ decode_mfma_kernel(DecodeArgs a) {
   const int st_begin = tok_begin >> 4;
   const int st_end = (tok_end + 15) >> 4;
   const int n_tiles = st_end - st_begin;
-  const int n_mine = n_tiles > w ? (n_tiles - w + 3) >> 2 : 0;
+  // the wave's tiles: tile0 + kStride * n for n < n_mine -- every tile of
+  // its partition (split), or every fourth tile of the context
+  constexpr int kStride = SPLIT ? 1 : kDecodeWaves;
+  const int tile0 = SPLIT ? st_begin : st_begin + w;
+  const int n_mine =
+      SPLIT ? n_tiles : (n_tiles > w ? (n_tiles - w + kDecodeWaves - 1) / kDecodeWaves : 0);
 
   // lane offsets inside a tile, in bytes (chunk c adds KSTEP*c for K, 256*c
   // for V): K row `col` (8-bit, D = 128: row 8c + col%8), V token group `grp`
@@ -128,6 +141,29 @@ decode_mfma_kernel(DecodeArgs a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The wave's state to its LDS slice: head col's row sum (the four lanes'
+  // shares added), maximum and weighted values; n-tile row m = 4*grp + i of
+  // head col is dim 32u + 2m + j (n-tile 2u+j, 16-bit caches) or 64u + 4m + j
+  // (n-tile 4u+j, 8-bit caches)
+  auto stage_state = [&]() {
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mm = 4 * grp + i;
+        const int d = F8 ? 64 * (nt / 4) + 4 * mm + nt % 4 : 32 * (nt / 2) + 2 * mm + nt % 2;
+        sm_o[w][col][d] = acc[nt][i];
+      }
+    if (grp == 0) {
+      sm_m[w][col] = m;
+      sm_l[w][col] = lt;
+    }
+  };
+
+
 
   auto load = [&](Tl &t, size_t tile_bytes) {
     const char *kp = kc + tile_bytes + koff;
@@ -164,8 +200,8 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[kk], sacc);
     }
 
-    const int t0 = (st_begin + w + 4 * n) * 16 + 4 * grp;
-    const bool tail = (st_begin + w + 4 * n) * 16 + 16 > tok_end;
+    const int t0 = (tile0 + kStride * n) * 16 + 4 * grp;
+    const bool tail = (tile0 + kStride * n) * 16 + 16 > tok_end;
     const int nvalid = tail ? max(0, min(4, tok_end - t0)) : 4;
     float sc[4];
 #pragma unroll
@@ -254,31 +290,36 @@ decode_mfma_kernel(DecodeArgs a) {
   // gqa70b 165 -> 154 us from one to three, 16-bit 278 -> 271 us from one
   // to two)
   if (n_mine > 0 && F8)
-    walk_tiles_n<Tl, 4>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+    walk_tiles_n<Tl, 4, kStride>(trow, tile0, n_mine, BS / 16, (unsigned)a.num_blocks,
                         (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
                         load, compute);
   else if (n_mine > 0)
-    walk_tiles_n<Tl, 3>(trow, st_begin + w, n_mine, BS / 16, (unsigned)a.num_blocks,
+    walk_tiles_n<Tl, 3, kStride>(trow, tile0, n_mine, BS / 16, (unsigned)a.num_blocks,
                         (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
                         load, compute);
 
-  // ---- merge the 4 wavefronts through LDS ----
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
-  // n-tile row m = 4*grp + i of head col is dim 32u + 2m + j (n-tile
-  // 2u+j, 16-bit caches) or 64u + 4m + j (n-tile 4u+j, 8-bit caches)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * grp + i;
-      const int d = F8 ? 64 * (nt / 4) + 4 * m + nt % 4 : 32 * (nt / 2) + 2 * m + nt % 2;
-      sm_o[w][col][d] = acc[nt][i];
+  stage_state();
+  if constexpr (SPLIT) {
+    // the wave's partial, row by row from its own LDS slice (written and
+    // read by this wave only: ordering inside the wave is all it needs),
+    // written through L2 (nothing in this kernel reads it); the partition
+    // is not empty, so each real head's maximum is finite
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int idx = lane; idx < G * D; idx += 64) {
+      const int hh = idx / D, d = idx % D;
+      const size_t pi = ((size_t)s * Hq + g * G + hh) * a.num_parts + part;
+      store_through(&a.ws_o[pi * D + d], sm_o[w][hh][d] * a.v_scale);
+      if (d == 0) {
+        store_through(&a.ws_m[pi], sm_m[w][hh]);
+        store_through(&a.ws_l[pi], sm_l[w][hh]);
+      }
     }
-  if (grp == 0) {
-    sm_m[w][col] = m;
-    sm_l[w][col] = lt;
+    return;
   }
+
+  // ---- merge the 4 wavefronts through LDS ----
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
     const int hh = idx / D, d = idx % D;
@@ -294,29 +335,22 @@ decode_mfma_kernel(DecodeArgs a) {
     }
     const int h = g * G + hh;
     num *= a.v_scale;  // value dequantisation (1 for 16-bit caches)
-    if constexpr (SPLIT) {
-      // partials written through L2 (nothing in this kernel reads them)
-      const size_t pi = ((size_t)s * Hq + h) * a.num_parts + part;
-      store_through(&a.ws_o[pi * D + d], num);
-      if (d == 0) {
-        store_through(&a.ws_m[pi], M);
-        store_through(&a.ws_l[pi], den);
-      }
-    } else {
-      store_elem<QT>(a.out, ((size_t)s * Hq + h) * D + d, num / den);
-    }
+    store_elem<QT>(a.out, ((size_t)s * Hq + h) * D + d, num / den);
   }
 }
 
 template <int QT, int CT, int D, int BS>
 static hipError_t launch_mfma(const DecodeArgs &a, bool split, hipStream_t st) {
-  dim3 grid(a.num_kv_heads, a.num_seqs, split ? a.num_parts : 1);
-  if (split)
+  if (split) {
+    // one wavefront per partition, four partitions per workgroup
+    const dim3 grid(a.num_kv_heads, a.num_seqs,
+                    (a.num_parts + kDecodeWaves - 1) / kDecodeWaves);
     hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, true>), grid,
                        dim3(kDecodeThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, false>), grid,
-                       dim3(kDecodeThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, false>),
+                     dim3(a.num_kv_heads, a.num_seqs, 1), dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -375,22 +375,11 @@ decode_vector_kernel(DecodeArgs a) {
 template <int QT, int CT, int D, int BS>
 static hipError_t launch_vec(const DecodeArgs &a, bool split, hipStream_t st) {
   if (split) {
-    // partitions per wave: enough that every wave of the grid is resident at
-    // once (about 16 waves per compute unit), at most kMaxPartsPerWave, and
-    // few enough that each of a workgroup's four waves gets some
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0) {
-      (void)hipGetLastError();  // a failed query must not read as a failed launch
-      cus = 256;
-    }
+    // every wave of the grid resident at once: 16 waves per compute unit
     const int64_t units = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
-    const int64_t resident = (int64_t)cus * 4 * kDecodeWaves;
-    int64_t ppw = (units + resident - 1) / resident;
-    ppw = std::min<int64_t>(ppw, std::max(1, a.num_parts / kDecodeWaves));
+    const int64_t resident = (int64_t)device_compute_units() * 4 * kDecodeWaves;
     DecodeArgs b = a;
-    b.parts_per_wave = (int)std::max<int64_t>(1, std::min<int64_t>(ppw, kMaxPartsPerWave));
+    b.parts_per_wave = split_parts_per_wave(units, resident, a.num_parts);
     const int per_wg = kDecodeWaves * b.parts_per_wave;
     const dim3 grid(a.num_heads, a.num_seqs, (a.num_parts + per_wg - 1) / per_wg);
     hipLaunchKernelGGL((decode_vector_kernel<QT, CT, D, BS, true>), grid,

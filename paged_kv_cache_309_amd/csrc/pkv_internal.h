@@ -16,6 +16,30 @@ constexpr int kDecodeWaves = 4;
 // Most partitions one wave of the vector kernel's split launch computes.
 constexpr int kMaxPartsPerWave = 4;
 
+// Compute units of the current device (256 if the query fails; a failed
+// query's error is cleared so that it cannot read as a failed launch).
+inline int device_compute_units() {
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
+}
+
+// Consecutive partitions one wavefront of a split launch computes: enough
+// that every wavefront of the grid (units = partitions to compute) is
+// resident at once, at most kMaxPartsPerWave, and at most a quarter of the
+// partitions so that each of a workgroup's four wavefronts gets some.
+inline int split_parts_per_wave(int64_t units, int64_t resident_waves, int num_parts) {
+  int64_t k = (units + resident_waves - 1) / resident_waves;
+  k = k < (int64_t)(num_parts / kDecodeWaves) ? k : (int64_t)(num_parts / kDecodeWaves);
+  k = k < (int64_t)kMaxPartsPerWave ? k : (int64_t)kMaxPartsPerWave;
+  return k < 1 ? 1 : (int)k;
+}
+
 struct DecodeArgs {
   void *out;              // [S, Hq, D] storage type (single pass, reduce)
   float *ws_o;            // [S, Hq, P, D] partial weighted sums (split)
@@ -36,8 +60,8 @@ struct DecodeArgs {
   int block_size;
   int part_tokens;        // tokens per partition (split); unused otherwise
   int num_parts;          // partitions per sequence (1 for single pass)
-  int parts_per_wave = 1; // split on the vector kernel: consecutive partitions
-                          // one wave computes (1 .. kMaxPartsPerWave)
+  int parts_per_wave = 1; // split on the vector kernel: consecutive
+                          // partitions one wavefront computes (1 .. 4)
   // multi-query (chunked prefill) on the vector kernel: q / out hold
   // num_query_tokens rows; sequence s's rows are query_start_loc[s] ..
   // query_start_loc[s+1]-1, the last tokens of its context (causal).
