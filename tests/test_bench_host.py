@@ -59,3 +59,25 @@ def test_digest_ignores_comments_not_code():
     assert bench._code_only(a) != bench._code_only(c)
     # a comment marker inside a string literal is code
     assert b"//" in bench._code_only(b'const char *u = "a//b";')
+
+
+def test_unique_kv_bytes_equal_logical_without_sharing():
+    import workloads as wl
+    w = wl.random_case(31, num_seqs=5, max_len=300, num_heads=4, num_kv_heads=2,
+                       head_dim=64, block_size=16, dtype="f16", pool_factor=1.5)
+    assert bench.unique_kv_bytes(w, 2) == w.kv_bytes()
+
+
+def test_unique_kv_bytes_count_a_shared_prefix_once():
+    """Sequences over one 64-token prefix: the prefix's tokens count once,
+    every sequence's own tokens once each."""
+    import numpy as np
+    import workloads as wl
+    lens = [70, 100, 65, 200]
+    w = wl.build("prefix", lens=lens, num_heads=2, num_kv_heads=2, head_dim=64,
+                 block_size=16, dtype="bf16", seed=3, pool_factor=1.0, prefix_len=64)
+    shared = w.block_tables[:, :4]
+    assert (shared == shared[0]).all()  # the prefix blocks are one set
+    tokens = 64 + sum(L - 64 for L in lens)
+    assert bench.unique_kv_bytes(w, 2) == tokens * 2 * 64 * 2 * 2
+    assert bench.unique_kv_bytes(w, 2) < w.kv_bytes()
