@@ -36,6 +36,13 @@
 //  * the next tile's loads are issued before the current tile is computed;
 //    the tile's address is a scalar, each lane's offset inside a tile is
 //    fixed for the whole loop;
+//  * tiles are streamed (non-temporal loads), except the leading blocks the
+//    neighbouring sequence's table maps to the same physical blocks - a
+//    shared prefix, which every sharer reads - whose plain loads keep them
+//    in cache.  The two kinds of tile are two walks, so the waits of each
+//    stay exact (a branch between load kinds per tile makes the compiler
+//    merge them or drain the next tile's loads).  128 sequences over one
+//    1024-token prefix, 32 heads: 201.8 -> 154.5 us;
 //  * at the end the 16 partial states (4 rows x 4 waves) are merged through
 //    LDS, each rescaled to the largest maximum;
 //  * split launches instead give each wave partitions of its own: wave w of
@@ -47,6 +54,7 @@
 //    states and writes the partials to the workspace.  The host picks k so
 //    that the whole grid is resident at once.
 #include <algorithm>
+#include <type_traits>
 
 #include "pkv_device.h"
 
@@ -173,21 +181,27 @@ decode_vector_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
 
-  auto load = [&](Tl &t, size_t tile_bytes) {
+  // one tile's loads: non-temporal (streamed), or plain for a block the
+  // neighbouring sequence shares, which the other sharers read too
+  auto load_with = [&](Tl &t, size_t tile_bytes, auto keep) {
+    constexpr bool KEEP = decltype(keep)::value;
     const char *kp = kc + tile_bytes + koff;
     const char *vp = vc + tile_bytes + voff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (Tl::KW == 1) {
-        t.k[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(kp + i * D * E));
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(kp + i * D * E);
+        if constexpr (KEEP) t.k[i][0] = *p;
+        else t.k[i][0] = __builtin_nontemporal_load(p);
       } else if constexpr (Tl::KW == 2) {
-        const u32x2 x = load_stream8(kp + i * D * E);
+        const u32x2 x = KEEP ? load_keep8(kp + i * D * E) : load_stream8(kp + i * D * E);
         t.k[i][0] = x[0];
         t.k[i][1] = x[1];
       } else {
 #pragma unroll
         for (int u = 0; u < Tl::KW / 4; ++u) {
-          const u32x4 x = load_stream16(kp + i * D * E + 16 * u);
+          const char *p = kp + i * D * E + 16 * u;
+          const u32x4 x = KEEP ? load_keep16(p) : load_stream16(p);
           t.k[i][4 * u + 0] = x[0];
           t.k[i][4 * u + 1] = x[1];
           t.k[i][4 * u + 2] = x[2];
@@ -197,13 +211,15 @@ decode_vector_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int ii = 0; ii < Tl::VI; ++ii) {
-      const u32x4 x = load_stream16(vp + ii * 256);
+      const u32x4 x = KEEP ? load_keep16(vp + ii * 256) : load_stream16(vp + ii * 256);
       t.v[4 * ii + 0] = x[0];
       t.v[4 * ii + 1] = x[1];
       t.v[4 * ii + 2] = x[2];
       t.v[4 * ii + 3] = x[3];
     }
   };
+  auto load = [&](Tl &t, size_t tile_bytes) { load_with(t, tile_bytes, std::false_type{}); };
+  auto load_keep = [&](Tl &t, size_t tile_bytes) { load_with(t, tile_bytes, std::true_type{}); };
 
   auto compute = [&](Tl &t, int n) {
     // ---- logits of this row's four tokens (log2 units) ----
@@ -301,10 +317,41 @@ decode_vector_kernel(DecodeArgs a) {
   };
 
   if (n_mine > 0) {
+    // Leading blocks the neighbouring sequence's table maps to the same
+    // physical blocks (the next sequence's; the previous one's for the
+    // last): a shared prefix, which sequences that share one sit side by
+    // side in a batch to make visible.  64 entries per step, stopping at the
+    // first that differs - at once for a sequence that shares nothing.
+    int shared_tiles = 0;
+    if (a.num_seqs > 1) {
+      const int32_t *tnb =
+          a.block_tables + (size_t)(s + 1 < a.num_seqs ? s + 1 : s - 1) * a.max_blocks;
+      const int nblk = (tok_end + BS - 1) / BS;
+      int j0 = 0;
+      for (; j0 < nblk; j0 += 64) {
+        const int j = j0 + lane;
+        const uint64_t differ = __builtin_amdgcn_ballot_w64(j < nblk && trow[j] != tnb[j]);
+        if (differ) {
+          j0 += (int)__builtin_ctzll(differ);
+          break;
+        }
+      }
+      shared_tiles = min(j0, nblk) * (BS / 16);
+    }
+    // the wave's tiles in front of shared_tiles are read with plain loads,
+    // the rest streamed; two walks, each with its own exact waits
+    const int n_keep =
+        min(n_mine, shared_tiles > tile0 ? (shared_tiles - tile0 + kStride - 1) / kStride : 0);
     constexpr size_t tile_elems = (size_t)16 * D;
-    walk_tiles<Tl, kStride>(trow, tile0, n_mine, BS / 16, (unsigned)a.num_blocks,
-                   (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, tile_elems * E,
-                   load, compute);
+    if (n_keep > 0)
+      walk_tiles<Tl, kStride>(trow, tile0, n_keep, BS / 16, (unsigned)a.num_blocks,
+                              (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E,
+                              tile_elems * E, load_keep, compute);
+    if (n_mine > n_keep)
+      walk_tiles<Tl, kStride>(trow, tile0 + kStride * n_keep, n_mine - n_keep, BS / 16,
+                              (unsigned)a.num_blocks, (size_t)g * BS * D * E,
+                              (size_t)Hkv * BS * D * E, tile_elems * E, load,
+                              [&](Tl &t, int n) { compute(t, n + n_keep); });
   }
 
   if constexpr (SPLIT) {

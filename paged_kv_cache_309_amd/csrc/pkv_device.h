@@ -133,6 +133,13 @@ __device__ __forceinline__ float row_sum16(float x) {
 __device__ __forceinline__ u32x4 load_stream16(const void *p) {
   return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
 }
+// Plain loads: the lines stay in cache for other readers.
+__device__ __forceinline__ u32x4 load_keep16(const void *p) {
+  return *static_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 load_keep8(const void *p) {
+  return *static_cast<const u32x2 *>(p);
+}
 __device__ __forceinline__ u32x2 load_stream8(const void *p) {
   return __builtin_nontemporal_load(static_cast<const u32x2 *>(p));
 }

@@ -343,3 +343,51 @@ def test_split_several_partitions_per_wave(i):
     kd, vd = dev.cache_from_host(kc, vc)
     got = to_f64(dev.decode(kd, vd, "split", part))
     compare(got, want, dtype, f"split{part} parts/wave={ppw}")
+
+
+@pytest.mark.parametrize("dtype,bs,prefix", [("bf16", 16, 80), ("f16", 32, 96),
+                                             ("f32", 16, 48)])
+def test_shared_prefix_reads_match_private_copies_bitwise(dtype, bs, prefix):
+    """Tiles of a prefix the neighbouring sequence's table shares are read
+    with cache-keeping loads, the rest streamed; the policy never touches
+    the arithmetic.  The same workload with every sequence but the first
+    given private copies of the prefix blocks (so nothing is shared) gives
+    bitwise the same outputs, single pass and split; a sequence in the
+    middle with a private prefix breaks the run of sharers; the outputs
+    match the oracle."""
+    lens = [prefix + x for x in (1, 37, 200, 3, 64, 150, 90)]
+    w = wl.build("prefix", lens=lens, num_heads=4, num_kv_heads=4, head_dim=128,
+                 block_size=bs, dtype=dtype, seed=17, pool_factor=3.0,
+                 prefix_len=prefix)
+    print_case("shared prefix", w)
+    nb = prefix // bs
+    assert (w.block_tables[:, :nb] == w.block_tables[0, :nb]).all()
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    # private copies of the prefix blocks in unused blocks of the pool
+    used = set(w.block_tables[w.block_tables >= 0].tolist())
+    free = [p for p in range(w.num_blocks) if p not in used]
+    assert len(free) >= nb * (w.num_seqs - 1)
+    private = w.block_tables.copy()
+    for s in range(1, w.num_seqs):
+        for j in range(nb):
+            p = free.pop()
+            kd[p] = kd[private[s, j]]
+            vd[p] = vd[private[s, j]]
+            private[s, j] = p
+    # a private-prefix sequence between sharers: sequence 3 keeps copies,
+    # the others go back to the shared blocks
+    mixed = w.block_tables.copy()
+    mixed[3] = private[3]
+    torch.cuda.synchronize()
+    for variant, part in (("single", 0), ("split", bs), ("split", 128)):
+        shared = dev.decode(kd, vd, variant, part).cpu()
+        priv = dev.decode(kd, vd, variant, part,
+                          tables=torch.from_numpy(private).cuda()).cpu()
+        mix = dev.decode(kd, vd, variant, part,
+                         tables=torch.from_numpy(mixed).cuda()).cpu()
+        assert torch.equal(shared, priv), variant
+        assert torch.equal(shared, mix), variant
+        compare(to_f64(shared), want, dtype, f"shared prefix {variant}{part}")
