@@ -317,27 +317,10 @@ decode_vector_kernel(DecodeArgs a) {
   };
 
   if (n_mine > 0) {
-    // Leading blocks the neighbouring sequence's table maps to the same
-    // physical blocks (the next sequence's; the previous one's for the
-    // last): a shared prefix, which sequences that share one sit side by
-    // side in a batch to make visible.  64 entries per step, stopping at the
-    // first that differs - at once for a sequence that shares nothing.
-    int shared_tiles = 0;
-    if (a.num_seqs > 1) {
-      const int32_t *tnb =
-          a.block_tables + (size_t)(s + 1 < a.num_seqs ? s + 1 : s - 1) * a.max_blocks;
-      const int nblk = (tok_end + BS - 1) / BS;
-      int j0 = 0;
-      for (; j0 < nblk; j0 += 64) {
-        const int j = j0 + lane;
-        const uint64_t differ = __builtin_amdgcn_ballot_w64(j < nblk && trow[j] != tnb[j]);
-        if (differ) {
-          j0 += (int)__builtin_ctzll(differ);
-          break;
-        }
-      }
-      shared_tiles = min(j0, nblk) * (BS / 16);
-    }
+    // tiles of a prefix the neighbouring sequence shares
+    const int shared_tiles =
+        shared_prefix_blocks<BS>(a.block_tables, a.max_blocks, a.num_seqs, s, tok_end, lane) *
+        (BS / 16);
     // the wave's tiles in front of shared_tiles are read with plain loads,
     // the rest streamed; two walks, each with its own exact waits
     const int n_keep =

@@ -240,6 +240,31 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
   return chosen;
 }
 
+// Leading blocks of a context of tok_end tokens that the neighbouring
+// sequence's table (the next sequence's; the previous one's for the last)
+// maps to the same physical blocks: a shared prefix, which every sharer
+// reads, so its tiles are read with loads that keep them in cache.
+// Sequences that share a prefix sit side by side in a batch.  64 entries
+// per step (one vector load of each table and a ballot), stopping at the
+// first entry that differs - at once for a sequence that shares nothing.
+// Wave-uniform.
+template <int BS>
+__device__ __forceinline__ int shared_prefix_blocks(const int32_t *block_tables,
+                                                    int max_blocks, int num_seqs, int s,
+                                                    int tok_end, int lane) {
+  if (num_seqs <= 1) return 0;
+  const int32_t *trow = block_tables + (size_t)s * max_blocks;
+  const int32_t *tnb = block_tables + (size_t)(s + 1 < num_seqs ? s + 1 : s - 1) * max_blocks;
+  const int nblk = (tok_end + BS - 1) / BS;
+  int j0 = 0;
+  for (; j0 < nblk; j0 += 64) {
+    const int j = j0 + lane;
+    const uint64_t differ = __builtin_amdgcn_ballot_w64(j < nblk && trow[j] != tnb[j]);
+    if (differ) return j0 + (int)__builtin_ctzll(differ);
+  }
+  return nblk;
+}
+
 // Walks the 16-token tiles a wavefront owns, with one tile of prefetch.
 //
 // The wave owns tiles k = k0 + STRIDE*n, n = 0 .. n_mine-1 (decode: k0 =
