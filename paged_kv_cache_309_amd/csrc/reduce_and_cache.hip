@@ -14,18 +14,20 @@ namespace pkv {
 // ceil(L / part_tokens) were empty and are not read.
 // One workgroup of 256 threads per (sequence, head): thread t takes the
 // four dims 4 (t % (D/4)) .. +3 of the partitions p = t / (D/4) (mod
-// 256 / (D/4)), as 16-byte loads of o_p; the partial sums of the partition
-// groups are added through LDS.
+// 256 / (D/4)), as 16-byte loads of o_p, in one pass with a running maximum
+// of its own (each partition's m_p, l_p and o_p are loaded together, the
+// loop unrolled so that the loads of several partitions are in flight);
+// the partition groups' states are merged through LDS, each rescaled to the
+// largest maximum.
 constexpr int kReduceThreads = 256;
 
 template <int DT, int D>
 __global__ void __launch_bounds__(kReduceThreads) partition_reduce_kernel(DecodeArgs a) {
   constexpr int Q = D / 4;                 // dim quads per row
   constexpr int PG = kReduceThreads / Q;   // partition groups
-  constexpr int W = kReduceThreads / 64;   // wavefronts
   __shared__ f32x4 sm_num[PG][Q];
   __shared__ float sm_den[PG];
-  __shared__ float sm_max[W];
+  __shared__ float sm_m[PG];
   const int h = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
   const int q = t % Q, pg = t / Q;
   const int Hq = a.num_heads;
@@ -38,35 +40,40 @@ __global__ void __launch_bounds__(kReduceThreads) partition_reduce_kernel(Decode
     for (int i = t; i < D; i += kReduceThreads) store_elem<DT>(a.out, orow + i, 0.f);
     return;
   }
-  // M = max_p m_p: a strided slice per thread, then the workgroup maximum
-  float M = -INFINITY;
-  for (int p = t; p < np; p += kReduceThreads) M = fmaxf(M, a.ws_m[base + p]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((t & 63) == 0) sm_max[t >> 6] = M;
-  __syncthreads();
-  M = sm_max[0];
-#pragma unroll
-  for (int i = 1; i < W; ++i) M = fmaxf(M, sm_max[i]);
-  // this thread's partitions
+  // this thread's partitions, in one pass: (m, num, den) rescaled to the
+  // running maximum m as partitions arrive (m = -inf: nothing yet, weight 0)
+  float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
+#pragma unroll 8
   for (int p = pg; p < np; p += PG) {
-    const float f = fast_exp2(a.ws_m[base + p] - M);
+    const float mp = a.ws_m[base + p];
+    const float lp = a.ws_l[base + p];
     const f32x4 o = *reinterpret_cast<const f32x4 *>(a.ws_o + (base + p) * D + 4 * q);
-    num += f * o;
-    den = fmaf(f, a.ws_l[base + p], den);
+    const float mn = fmaxf(m, mp);
+    const float r = fast_exp2(m - mn), f = fast_exp2(mp - mn);
+    num = r * num + f * o;
+    den = fmaf(r, den, f * lp);
+    m = mn;
   }
   sm_num[pg][q] = num;
-  if (q == 0) sm_den[pg] = den;
+  if (q == 0) {
+    sm_den[pg] = den;
+    sm_m[pg] = m;
+  }
   __syncthreads();
   if (pg == 0) {
-    f32x4 n = sm_num[0][q];
-    float dd = sm_den[0];
+    // M: the largest partition maximum (finite: np >= 1); a group without
+    // partitions has m = -inf and weight 0
+    float M = sm_m[0];
 #pragma unroll
-    for (int i = 1; i < PG; ++i) {
-      n += sm_num[i][q];
-      dd += sm_den[i];
+    for (int i = 1; i < PG; ++i) M = fmaxf(M, sm_m[i]);
+    f32x4 n = {0.f, 0.f, 0.f, 0.f};
+    float dd = 0.f;
+#pragma unroll
+    for (int i = 0; i < PG; ++i) {
+      const float f = fast_exp2(sm_m[i] - M);
+      n += f * sm_num[i][q];
+      dd = fmaf(f, sm_den[i], dd);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_elem<DT>(a.out, orow + 4 * q + e, n[e] / dd);
