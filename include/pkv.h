@@ -87,7 +87,7 @@ typedef enum pkv_status {
                               block_size */
   PKV_ERR_WORKSPACE = 9,   /* workspace NULL or smaller than required */
   PKV_ERR_LAUNCH = 10,     /* the HIP runtime rejected a kernel launch */
-  PKV_ERR_ALIAS = 11,      /* out overlaps an input */
+  PKV_ERR_ALIAS = 11,      /* out (or a workspace) overlaps an input */
   PKV_ERR_SCALE = 16       /* a dequantisation scale not finite and > 0 */
 } pkv_status;
 
@@ -249,10 +249,11 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache,
  * fraction; magnitudes of 448 and beyond saturate to +-448; NaN stays NaN).
  * paged_attention_decode_fp8 / _split_fp8: attention over the dequantised
  * keys and values; the key scale multiplies the logits and the value scale
- * the output, both in fp32.  The grouped-query matrix-core path needs a
- * 16-bit dims->dtype (fp32 q with Hq/Hkv in 2..16 returns PKV_ERR_DTYPE).
- * Scales must be finite and > 0 (else PKV_ERR_SCALE).  Everything else is
- * as for the calls above. */
+ * the output, both in fp32.  fp16/bf16 queries with Hq/Hkv in 2..16 run on
+ * the matrix cores (codes widened exactly to the query's type); every
+ * other case, fp32 queries with any Hq/Hkv included, runs on the vector
+ * ALUs with the codes widened to fp32.  Scales must be finite and > 0
+ * (else PKV_ERR_SCALE).  Everything else is as for the calls above. */
 int reshape_and_cache_fp8(const void *k, const void *v, void *k_cache,
                           void *v_cache, const int64_t *slot_mapping,
                           int num_tokens, int block_size, float k_scale,

@@ -90,6 +90,65 @@ def _is_fp8(cache: torch.Tensor) -> bool:
     return cache.dtype == torch.float8_e4m3fn
 
 
+# Shape and dtype checks.  The C ABI sizes its checks and the kernels address
+# memory from the dims struct alone, so every tensor is checked against
+# those dims here, before any launch: a mismatch raises ValueError.
+def _expect(t, name: str, shape=None, dtypes=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtypes is not None and t.dtype not in dtypes:
+        want = ", ".join(str(d) for d in dtypes)
+        raise ValueError(f"{name} has dtype {t.dtype}; expected {want}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+
+
+def _rank(t, name: str, n: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _pools(k_cache, v_cache, elem_dtype, head_dim=None, num_kv_heads=None):
+    """Checks a (k_cache, v_cache) pair against the block layouts and the
+    element type of the values it caches (or E4M3); returns (NB, Hkv, bs,
+    D)."""
+    _rank(k_cache, "k_cache", 4)
+    NB, Hkv, bs, D = k_cache.shape
+    _expect(k_cache, "k_cache", dtypes=(elem_dtype, torch.float8_e4m3fn))
+    if head_dim is not None and D != head_dim:
+        raise ValueError(f"k_cache has head_dim {D}; the queries/values have {head_dim}")
+    if num_kv_heads is not None and Hkv != num_kv_heads:
+        raise ValueError(f"k_cache has {Hkv} KV heads; the new keys have {num_kv_heads}")
+    if bs % 4:
+        raise ValueError(f"block size {bs} is not a multiple of 4")
+    _expect(v_cache, "v_cache", shape=(NB, Hkv, bs // 4, D, 4), dtypes=(k_cache.dtype,))
+    return NB, Hkv, bs, D
+
+
+def _block_size(block_size, bs: int) -> int:
+    if block_size is not None and int(block_size) != bs:
+        raise ValueError(f"block_size {block_size} differs from the cache's {bs}")
+    return bs
+
+
+def _decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens,
+                   block_size) -> tuple:
+    """Checks the tensors of a decode call; returns (dims, block size)."""
+    _rank(q, "q", 3)
+    _expect(q, "q", dtypes=tuple(_DTYPES))
+    S, Hq, D = q.shape
+    _expect(out, "out", shape=(S, Hq, D), dtypes=(q.dtype,))
+    NB, Hkv, bs, _ = _pools(k_cache, v_cache, q.dtype, head_dim=D)
+    bs = _block_size(block_size, bs)
+    _rank(block_tables, "block_tables", 2)
+    _expect(block_tables, "block_tables", shape=(S, block_tables.shape[1]),
+            dtypes=(torch.int32,))
+    _expect(context_lens, "context_lens", shape=(S,), dtypes=(torch.int32,))
+    return PkvDims(S, Hq, Hkv, D, NB, block_tables.shape[1], _dtype(q)), bs
+
+
 def _dims(q: torch.Tensor, k_cache: torch.Tensor,
           block_tables: torch.Tensor) -> PkvDims:
     S, Hq, D = q.shape
@@ -103,9 +162,13 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor,
                       k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Write k[i], v[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64);
     8-bit caches store the E4M3 value nearest to x / scale."""
-    _on_one_device(k, v, k_cache, v_cache, slot_mapping, stream=stream)
+    _rank(k, "k", 3)
+    _expect(k, "k", dtypes=tuple(_DTYPES))
     T, Hkv, D = k.shape
-    NB, bs = k_cache.shape[0], k_cache.shape[2]
+    _expect(v, "v", shape=(T, Hkv, D), dtypes=(k.dtype,))
+    NB, _, bs, _ = _pools(k_cache, v_cache, k.dtype, head_dim=D, num_kv_heads=Hkv)
+    _expect(slot_mapping, "slot_mapping", shape=(T,), dtypes=(torch.int64,))
+    _on_one_device(k, v, k_cache, v_cache, slot_mapping, stream=stream)
     dims = PkvDims(0, Hkv, Hkv, D, NB, 0, _dtype(k))
     if _is_fp8(k_cache):
         _lib.check(_lib.lib().reshape_and_cache_fp8(
@@ -127,9 +190,9 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor,
                            v_scale: float = 1.0) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K) V over context_lens[s]
     tokens reached through block_tables[s]; single launch."""
+    dims, bs = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                              context_lens, block_size)
     _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens, stream=stream)
-    bs = block_size or k_cache.shape[2]
-    dims = _dims(q, k_cache, block_tables)
     if _is_fp8(k_cache):
         _lib.check(_lib.lib().paged_attention_decode_fp8(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -147,7 +210,10 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor,
 def split_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor,
                           block_tables: torch.Tensor, partition_size: int,
                           block_size: int | None = None) -> int:
-    bs = block_size or k_cache.shape[2]
+    _rank(q, "q", 3)
+    _rank(k_cache, "k_cache", 4)
+    _rank(block_tables, "block_tables", 2)
+    bs = _block_size(block_size, k_cache.shape[2])
     dims = _dims(q, k_cache, block_tables)
     n = ctypes.c_size_t(0)
     _lib.check(_lib.lib().paged_attention_split_workspace_bytes(
@@ -167,10 +233,11 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
     """Same result as paged_attention_decode, in two launches: per-partition
     partials into `workspace` (a device byte tensor of at least
     split_workspace_bytes(...)), then the partition reduce."""
+    dims, bs = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                              context_lens, block_size)
+    _expect(workspace, "workspace")
     _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens, workspace,
                    stream=stream)
-    bs = block_size or k_cache.shape[2]
-    dims = _dims(q, k_cache, block_tables)
     if _is_fp8(k_cache):
         _lib.check(_lib.lib().paged_attention_decode_split_fp8(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -200,14 +267,22 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor,
     sequence (rows query_start_loc[s] .. query_start_loc[s+1]-1, the last
     tokens of its context, whose K/V are already in the cache); each
     attends causally.  max_query_len bounds every chunk (default T)."""
+    _rank(q, "q", 3)
+    _expect(q, "q", dtypes=tuple(_DTYPES))
+    T, Hq, D = q.shape
+    _expect(out, "out", shape=(T, Hq, D), dtypes=(q.dtype,))
+    NB, Hkv, bs, _ = _pools(k_cache, v_cache, q.dtype, head_dim=D)
+    bs = _block_size(block_size, bs)
+    _rank(context_lens, "context_lens", 1)
+    _expect(context_lens, "context_lens", dtypes=(torch.int32,))
+    S = context_lens.shape[0]
+    _rank(block_tables, "block_tables", 2)
+    _expect(block_tables, "block_tables", shape=(S, block_tables.shape[1]),
+            dtypes=(torch.int32,))
+    _expect(query_start_loc, "query_start_loc", shape=(S + 1,), dtypes=(torch.int32,))
     _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens,
                    query_start_loc, stream=stream)
-    T = q.shape[0]
-    bs = block_size or k_cache.shape[2]
-    S = context_lens.shape[0]
-    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    dims = PkvDims(S, q.shape[1], Hkv, q.shape[2], NB, block_tables.shape[1],
-                   _dtype(q))
+    dims = PkvDims(S, Hq, Hkv, D, NB, block_tables.shape[1], _dtype(q))
     mq = T if max_query_len is None else int(max_query_len)
     if _is_fp8(k_cache):
         _lib.check(_lib.lib().paged_attention_prefill_fp8(
@@ -227,9 +302,15 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
                 block_mapping: torch.Tensor, stream=None) -> None:
     """Copy-on-write: block block_mapping[i, 1] of both caches becomes a
     copy of block block_mapping[i, 0] (device int64 [n, 2])."""
+    _rank(k_cache, "k_cache", 4)
+    if k_cache.dtype not in _DTYPES and not _is_fp8(k_cache):
+        raise ValueError(f"k_cache has unsupported dtype {k_cache.dtype}")
+    NB, Hkv, bs, D = _pools(k_cache, v_cache, k_cache.dtype)
+    _rank(block_mapping, "block_mapping", 2)
+    _expect(block_mapping, "block_mapping", shape=(block_mapping.shape[0], 2),
+            dtypes=(torch.int64,))
     _on_one_device(k_cache, v_cache, *([block_mapping] if block_mapping.numel() else []),
                    stream=stream)
-    NB, Hkv, bs, D = k_cache.shape
     dt = _lib.PKV_E4M3 if _is_fp8(k_cache) else _dtype(k_cache)
     dims = PkvDims(0, Hkv, Hkv, D, NB, 0, dt)
     n = block_mapping.shape[0] if block_mapping.numel() else 0
@@ -245,9 +326,17 @@ def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor,
     block_mapping[i, 0] of (src_k, src_v); each pool is on the GPU or in
     pinned host memory, and the mapping (int64 [n, 2]) on the GPU or pinned.
     Asynchronous: synchronise the stream before reading a host pool."""
+    _rank(src_k, "src_k", 4)
+    if src_k.dtype not in _DTYPES and not _is_fp8(src_k):
+        raise ValueError(f"src_k has unsupported dtype {src_k.dtype}")
+    NB, Hkv, bs, D = _pools(src_k, src_v, src_k.dtype)
+    _rank(dst_k, "dst_k", 4)
     if src_k.dtype != dst_k.dtype or src_k.shape[1:] != dst_k.shape[1:]:
         raise ValueError("source and destination pools differ in shape")
-    NB, Hkv, bs, D = src_k.shape
+    _pools(dst_k, dst_v, dst_k.dtype)
+    _rank(block_mapping, "block_mapping", 2)
+    _expect(block_mapping, "block_mapping", shape=(block_mapping.shape[0], 2),
+            dtypes=(torch.int64,))
     dt = _lib.PKV_E4M3 if _is_fp8(src_k) else _dtype(src_k)
     dims = PkvDims(0, Hkv, Hkv, D, 0, 0, dt)
     n = block_mapping.shape[0] if block_mapping.numel() else 0

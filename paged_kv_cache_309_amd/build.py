@@ -40,11 +40,13 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-file additions.  The matrix-core prefill's softmax maxima never see a
-# NaN (logits of masked and out-of-context tokens are set to -inf before the
-# maximum, and values past the context are zeroed bitwise), so its compile
-# may drop the NaN quieting around every max: about 18 fewer vector
-# instructions per 32-token step.  Infinities are still honoured.
+# Per-file additions.  No float operation of the matrix-core prefill sees a
+# NaN when q and the attended tokens' keys and values are finite: the keys
+# and values of tokens past the context (which may hold anything) are zeroed
+# bitwise before any float operation reads them, and the logits of masked
+# tokens are set to -inf before the maximum.  So its compile may drop the
+# NaN quieting around every max: about 18 fewer vector instructions per
+# 32-token step.  Infinities are still honoured.
 FILE_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
 
 

@@ -131,7 +131,8 @@ pkv::DecodeArgs make_args(void *out, const void *q, const void *k_cache,
 }
 
 // Matrix cores when a KV head serves 2..16 query heads in fp16/bf16; the
-// vector kernel otherwise.
+// vector kernel otherwise: multi-head attention, wider groups, and fp32
+// queries over any cache (fp32 arithmetic throughout, 8-bit caches too).
 bool use_mfma(const pkv_dims *d) {
   const int G = d->num_heads / d->num_kv_heads;
   return d->dtype != PKV_F32 && G >= 2 && G <= 16;
@@ -209,8 +210,6 @@ int decode(void *out, const void *q, const void *k_cache, const void *v_cache,
   int rc = check_decode(dims, block_size, &qb, &cb, cache_dtype == kCacheSame ? 0 : 1);
   if (rc != PKV_OK) return rc;
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
-  if (cache_dtype != kCacheSame && dims->dtype == PKV_F32 && use_mfma(dims))
-    return PKV_ERR_DTYPE;
   if (dims->num_seqs == 0) return PKV_OK;
   rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
   if (rc != PKV_OK) return rc;
@@ -307,8 +306,6 @@ int decode_split(void *out, const void *q, const void *k_cache, const void *v_ca
   int rc = check_decode(dims, block_size, &qb, &cb, cache_dtype == kCacheSame ? 0 : 1);
   if (rc != PKV_OK) return rc;
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_ERR_SCALE;
-  if (cache_dtype != kCacheSame && dims->dtype == PKV_F32 && use_mfma(dims))
-    return PKV_ERR_DTYPE;
   rc = split_ws_bytes(dims, block_size, partition_size, &need);
   if (rc != PKV_OK) return rc;
   if (dims->num_seqs == 0) return PKV_OK;
@@ -317,7 +314,10 @@ int decode_split(void *out, const void *q, const void *k_cache, const void *v_ca
   if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;
   if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb) ||
-      overlap(workspace, need, k_cache, cb) || overlap(workspace, need, v_cache, cb))
+      overlap(workspace, need, k_cache, cb) || overlap(workspace, need, v_cache, cb) ||
+      overlap(workspace, need, block_tables,
+              (size_t)dims->num_seqs * (size_t)dims->max_blocks_per_seq * 4) ||
+      overlap(workspace, need, context_lens, (size_t)dims->num_seqs * 4))
     return PKV_ERR_ALIAS;
 
   pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables,

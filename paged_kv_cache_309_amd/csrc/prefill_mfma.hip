@@ -249,6 +249,24 @@ prefill_mfma_kernel(PrefillArgs a) {
   const uint32_t one2 = Ops::pack2(1.f, 1.f);
   const u32x4 ones = {one2, one2, one2, one2};
 
+  // Key rows of tokens at or past L may hold anything, NaN included (stale
+  // blocks, or the stand-in block 0 of a tile past the context).  This
+  // lane's key operands are token row `col` of each tile: they are zeroed
+  // bitwise before any float operation sees them, so every value that
+  // reaches the logit products and the maxima is finite or -inf (the file
+  // is compiled without NaN semantics, which holds by this construction for
+  // finite q, K and V of the attended tokens).
+  auto zero_tail_keys = [&](auto &kw, int n) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (32 * n + 16 * st + col >= L) {
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(kw[st]) / sizeof(kw[st][0])); ++i)
+          kw[st][i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
   // stage = n % S; MAY_TAIL: the super-tile may reach past L
   auto compute = [&](int n, int stage, auto may_tail) {
     constexpr bool MAY_TAIL = decltype(may_tail)::value;
@@ -275,6 +293,7 @@ prefill_mfma_kernel(PrefillArgs a) {
         vraw[u][0] = lds16(v0);
         vraw[u][1] = lds16(v0 + RG::PIECE);
       }
+      if (MAY_TAIL && 32 * n + 32 > L) zero_tail_keys(kraw, n);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -293,6 +312,7 @@ prefill_mfma_kernel(PrefillArgs a) {
           const int c = kk * 4 + grp;
           kop[st][kk] = lds16(base + st * RG::PIECE + col * RG::ROWB + ((c ^ RG::key(col)) * 16));
         }
+      if (MAY_TAIL && 32 * n + 32 > L) zero_tail_keys(kop, n);
       // value operand of n-tile 2u+j: dim 32u + 2*col + j, four tokens of
       // tile 0 then the same four of tile 1 (8 bytes each, one piece apart,
       // so one two-address LDS read fills the operand's registers in place)

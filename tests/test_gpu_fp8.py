@@ -74,6 +74,7 @@ CASES = [
     ("f16", 32, 16, 2, 128, 4, 500, 1.0, 1.0),      # MFMA, bs 32
     ("bf16", 16, 12, 3, 64, 5, 300, 0.5, 2.0),      # MFMA, D 64
     ("f32", 16, 40, 2, 64, 3, 200, 1.0, 1.0),       # 20 per KV head: vector
+    ("f32", 16, 16, 2, 128, 4, 400, 0.5, 1.5),      # fp32 q, 8 per KV head: vector
 ]
 
 

@@ -11,8 +11,7 @@ Each case draws its own shape and data from its seed:
 Decode (single pass and split) and chunked prefill must match the oracle
 within the output type's tolerance.  The sweep reaches both decode kernels
 and the prefill kernel, which the group width and the types select.  fp32
-queries with a matrix-core-sized group over an 8-bit cache are rejected by
-the library and are not drawn.
+queries run on the vector kernel over either cache at every group width.
 """
 import numpy as np
 import pytest
@@ -32,10 +31,7 @@ def draw(seed):
     dt = ["f16", "bf16", "f32"][rng.integers(0, 3)]
     G = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 20]))
     Hkv = int(rng.integers(1, 5))
-    if dt == "f32" and 2 <= G <= 16:
-        cache = "same"
-    else:
-        cache = "fp8" if rng.random() < 0.5 else "same"
+    cache = "fp8" if rng.random() < 0.5 else "same"
     D = int(rng.choice([64, 128]))
     bs = int(rng.choice([16, 32]))
     ks = float(rng.uniform(0.1, 4.0)) if cache == "fp8" else 1.0
