@@ -88,7 +88,9 @@ typedef enum pkv_status {
   PKV_ERR_WORKSPACE = 9,   /* workspace NULL or smaller than required */
   PKV_ERR_LAUNCH = 10,     /* the HIP runtime rejected a kernel launch */
   PKV_ERR_ALIAS = 11,      /* out (or a workspace) overlaps an input */
-  PKV_ERR_SCALE = 16       /* a dequantisation scale not finite and > 0 */
+  PKV_ERR_SCALE = 16,      /* a dequantisation scale not finite and > 0 */
+  PKV_ERR_SCRATCH = 20     /* the split partials would not fit the static
+                              scratch of paged_attention_decode_split_static */
 } pkv_status;
 
 /* Sizes of one call.  Fields a call does not use are ignored. */
@@ -285,6 +287,35 @@ int paged_attention_decode_split_fp8(void *out, const void *q,
                                      void *workspace, size_t workspace_bytes,
                                      float k_scale, float v_scale,
                                      const pkv_dims *dims, pkv_stream_t stream);
+
+/*
+ * paged_attention_decode_split_static - paged_attention_decode_split with no
+ * workspace argument and no allocation of any kind, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, serving
+ * loops that forbid hipMalloc, harnesses that do not allow it.
+ *
+ * The partials live in a scratch array of PKV_STATIC_SCRATCH_BYTES (32 MiB)
+ * that the library holds on every device it runs on, from the first such
+ * call on that device until the process ends; the call uses the copy of the
+ * current device (the stream must belong to it).  Sizes whose partials need
+ * more (paged_attention_split_workspace_bytes > PKV_STATIC_SCRATCH_BYTES)
+ * return PKV_ERR_SCRATCH before anything is enqueued: 8 sequences x 32 heads
+ * x 32768 tokens at 512-token partitions need 8.1 MiB, 8 x 64 heads 16.3 MiB.
+ * No scratch byte needs a particular value on entry (every partial the
+ * merge reads is written by the same call), so the contents left by earlier
+ * calls do not matter.  Every call on one device shares its array: calls
+ * that overlap in time on one device (concurrent streams, or host threads
+ * with different streams) race on it and may return wrong results; calls
+ * ordered on one stream do not.  16-bit and fp32 caches only.  Arguments,
+ * results and every other error are those of paged_attention_decode_split.
+ */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int paged_attention_decode_split_static(void *out, const void *q, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens, float scale,
+                                        int block_size, int partition_size,
+                                        const pkv_dims *dims, pkv_stream_t stream);
 
 /* A static, human-readable description of a status code. */
 const char *pkv_status_string(int status);

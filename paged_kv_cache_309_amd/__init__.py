@@ -20,10 +20,11 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import PkvDims, PkvError
+from ._lib import STATIC_SCRATCH_BYTES, PkvDims, PkvError
 
 __all__ = ["reshape_and_cache", "paged_attention_decode",
            "paged_attention_decode_split", "split_workspace_bytes",
+           "paged_attention_decode_split_static", "STATIC_SCRATCH_BYTES",
            "paged_attention_prefill", "new_kv_cache", "copy_blocks",
            "swap_blocks", "BlockManager", "PkvError", "version"]
 
@@ -250,6 +251,31 @@ def paged_attention_decode_split(out: torch.Tensor, q: torch.Tensor,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), bs, int(partition_size),
         _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(dims), _stream(stream)))
+    return out
+
+
+def paged_attention_decode_split_static(out: torch.Tensor, q: torch.Tensor,
+                                        k_cache: torch.Tensor,
+                                        v_cache: torch.Tensor,
+                                        block_tables: torch.Tensor,
+                                        context_lens: torch.Tensor,
+                                        scale: float, partition_size: int,
+                                        block_size: int | None = None,
+                                        stream=None) -> torch.Tensor:
+    """paged_attention_decode_split without a workspace: the partials go to
+    the library's static per-device scratch (STATIC_SCRATCH_BYTES), so the
+    call allocates nothing.  Calls that overlap in time on one device race
+    on that scratch.  16-bit and fp32 caches."""
+    dims, bs = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                              context_lens, block_size)
+    if _is_fp8(k_cache):
+        raise ValueError("paged_attention_decode_split_static takes 16-bit "
+                         "or fp32 caches only")
+    _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens, stream=stream)
+    _lib.check(_lib.lib().paged_attention_decode_split_static(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), bs, int(partition_size),
         ctypes.byref(dims), _stream(stream)))
     return out
 

@@ -20,7 +20,11 @@ STATUS = {
     12: "PKV_ERR_NO_BLOCKS", 13: "PKV_ERR_UNKNOWN_SEQ",
     14: "PKV_ERR_SEQ_EXISTS", 15: "PKV_ERR_CAPACITY", 16: "PKV_ERR_SCALE",
     17: "PKV_ERR_SWAPPED", 18: "PKV_ERR_SHARED", 19: "PKV_ERR_MEMORY",
+    20: "PKV_ERR_SCRATCH",
 }
+
+# bytes of the static scratch paged_attention_decode_split_static uses
+STATIC_SCRATCH_BYTES = 32 << 20
 
 # every function include/*.h declares
 EXPORTS = ("reshape_and_cache", "paged_attention_decode",
@@ -35,7 +39,8 @@ EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "swap_blocks", "pkv_bm_create_with_host", "pkv_bm_swap_out",
            "pkv_bm_swap_in", "pkv_bm_num_free_host_blocks",
            "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table",
-           "paged_attention_prefill", "paged_attention_prefill_fp8")
+           "paged_attention_prefill", "paged_attention_prefill_fp8",
+           "paged_attention_decode_split_static")
 
 
 class PkvDims(ctypes.Structure):
@@ -127,6 +132,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_bm_is_swapped.argtypes = [P, I64]
     lib.pkv_bm_block_table.restype = I
     lib.pkv_bm_block_table.argtypes = [P, I64, P, I32, ctypes.POINTER(I32)]
+    lib.paged_attention_decode_split_static.restype = I
+    lib.paged_attention_decode_split_static.argtypes = [P, P, P, P, P, P, F, I,
+                                                        I, D, P]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_version.restype = I

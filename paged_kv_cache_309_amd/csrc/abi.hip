@@ -5,6 +5,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pkv.h"
 #include "pkv_blocks.h"
 #include "pkv_internal.h"
@@ -342,6 +344,41 @@ int decode_split(void *out, const void *q, const void *k_cache, const void *v_ca
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+// ---- the allocation-free split decode's scratch ----------------------------
+// For callers that cannot allocate device memory.  The split partials of
+// paged_attention_decode_split_static live in this array; every device the
+// library runs on holds its own copy (at its own address) until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the per-device address from
+// hipGetSymbolAddress instead.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current).
+int static_scratch(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PKV_ERR_LAUNCH;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,6 +471,29 @@ int paged_attention_decode_split_fp8(void *out, const void *q, const void *k_cac
   return decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                       block_size, partition_size, workspace, workspace_bytes, dims, stream,
                       pkv::DT_FP8, k_scale, v_scale);
+}
+
+int paged_attention_decode_split_static(void *out, const void *q, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens, float scale,
+                                        int block_size, int partition_size,
+                                        const pkv_dims *dims, pkv_stream_t stream) {
+  // every check on plain arguments first (no HIP call before them)
+  size_t qb = 0, cb = 0, need = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  rc = split_ws_bytes(dims, block_size, partition_size, &need);
+  if (rc != PKV_OK) return rc;
+  if (need > (size_t)PKV_STATIC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  void *ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != PKV_OK) return rc;
+  return decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      block_size, partition_size, ws, (size_t)PKV_STATIC_SCRATCH_BYTES, dims,
+                      stream, kCacheSame, 1.f, 1.f);
 }
 
 int copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
@@ -539,6 +599,9 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_SWAPPED: return "sequence is swapped out (or, for swap_in, is not)";
     case PKV_ERR_SHARED: return "a block is shared with a sequence outside the list";
     case PKV_ERR_MEMORY: return "a pointer is neither device memory nor pinned host memory";
+    case PKV_ERR_SCRATCH:
+      return "the split partials need more than the library's static scratch "
+             "(PKV_STATIC_SCRATCH_BYTES, 32 MiB per device)";
     default: return "unknown status";
   }
 }

@@ -254,6 +254,36 @@ def test_fp32_queries_over_e4m3_pass_validation_at_every_group_size():
         assert rc == ERR["PKV_ERR_ALIGN"], (hq, hkv, S.get(rc))
 
 
+def test_static_split_checks_before_any_hip_call():
+    """The allocation-free split: every plain-argument check, the scratch
+    size included, returns before the runtime is asked for the scratch."""
+    lib = _lib.lib()
+
+    def st(d, bs=16, part=512, out=A, q=B):
+        return lib.paged_attention_decode_split_static(
+            out, q, C, DQ, E, F, 0.1, bs, part, ctypes.byref(d), None)
+    d = dims()
+    assert st(d, bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
+    assert st(dims(dt=3)) == ERR["PKV_ERR_DTYPE"]
+    assert st(dims(Hq=6, Hkv=4)) == ERR["PKV_ERR_HEADS"]
+    assert st(d, part=100) == ERR["PKV_ERR_PARTITION"]
+    assert st(d, out=None) == ERR["PKV_ERR_NULL"]
+    assert st(d, q=B + 4) == ERR["PKV_ERR_ALIGN"]
+    assert st(d, out=B + 16) == ERR["PKV_ERR_ALIAS"]
+    # 8 sequences x 64 heads x 32768 tokens: 256 partitions of 128 tokens
+    # need 8*64*256*130*4 B = 65 MiB of partials (refused); 64 of 512 tokens
+    # need 16.3 MiB (accepted: the NULL out is the next error)
+    big = dims(S_=8, Hq=64, Hkv=8, MB=2048)
+    need = ctypes.c_size_t(0)
+    assert lib.paged_attention_split_workspace_bytes(
+        ctypes.byref(big), 16, 128, ctypes.byref(need)) == 0
+    assert need.value == 8 * 64 * 256 * 130 * 4 > _lib.STATIC_SCRATCH_BYTES
+    assert st(big, part=128) == ERR["PKV_ERR_SCRATCH"]
+    assert st(big, part=512, out=None) == ERR["PKV_ERR_NULL"]
+    assert st(dims(S_=0), out=None, q=None) == 0
+    assert b"32 MiB" in lib.pkv_status_string(ERR["PKV_ERR_SCRATCH"])
+
+
 def _host_tensors(S_=2, H=2, Hkv=2, D=64, NB=4, bs=16, dt=None):
     import torch
     dt = dt or torch.float16
