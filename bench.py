@@ -56,7 +56,10 @@ def parse():
                             "shared_prefix_bs16", "shared_prefix_bs32",
                             "prefill70b", "prefill13b"],
                    help="default: mha13b (decode), prefill70b (prefill)")
-    p.add_argument("--variant", default="single", choices=["single", "split"])
+    p.add_argument("--variant", default="single",
+                   choices=["single", "split", "shared"],
+                   help="single-pass, split (partitions + reduce), or shared "
+                        "(each sharer set's prefix computed once)")
     p.add_argument("--partition", type=int, default=512)
     p.add_argument("--kv-dtype", default="same", choices=["same", "fp8"],
                    help="cache element type: the workload's (default) or "
@@ -205,6 +208,8 @@ def main():
            "bf16": torch.bfloat16}[w.dtype]
     fp8 = args.kv_dtype == "fp8"
     cdt = torch.float8_e4m3fn if fp8 else tdt
+    if args.variant == "shared" and (fp8 or w.dtype == "f32"):
+        raise SystemExit("--variant shared takes 16-bit caches and queries")
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -226,9 +231,22 @@ def main():
     del kk, vv
     out = torch.empty_like(q)
     ws = None
+    plan = None
+    plan_ms = None
     if args.variant == "split":
         nbytes = pkv.split_workspace_bytes(q, k_cache, tables, args.partition)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    elif args.variant == "shared":
+        # the sharer sets, found on the host from the host tables (built by
+        # the harness like the tables themselves; timed apart)
+        t_plan = time.perf_counter()
+        plan = pkv.PrefixPlan(w.block_tables, w.context_lens, w.block_size)
+        plan_ms = (time.perf_counter() - t_plan) * 1e3
+        nbytes = pkv.shared_prefix_workspace_bytes(q, k_cache, tables, plan)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        log(f"[bench] prefix plan: {plan.info.num_groups} sets, "
+            f"{plan.info.num_members} members, prefix "
+            f"{plan.info.max_prefix_tokens} tokens, built in {plan_ms:.3f} ms")
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.time()-t0:.1f}s")
 
@@ -245,6 +263,10 @@ def main():
         if args.variant == "single":
             pkv.paged_attention_decode(out, q, k_cache, v_cache, tables, lens,
                                        w.scale)
+        elif args.variant == "shared":
+            pkv.paged_attention_decode_shared_prefix(out, q, k_cache, v_cache,
+                                                     tables, lens, w.scale,
+                                                     plan, ws)
         else:
             pkv.paged_attention_decode_split(out, q, k_cache, v_cache, tables,
                                              lens, w.scale, args.partition, ws)
@@ -300,8 +322,10 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": stored_traffic(kernel, tag),
-                "kernel": kernel + ("" if args.variant == "single"
-                                    else " + partition_reduce_kernel"),
+                "kernel": ("prefill_mfma_kernel (prefix partials) + " if
+                           args.variant == "shared" else "") + kernel +
+                          {"single": "", "shared": "",
+                           "split": " + partition_reduce_kernel"}[args.variant],
                 "algorithmic_bytes_per_launch": att_alg_bytes,
                 "mean_launch_ms": round(att_mean_ms, 5),
                 "logical_kv_gbs": round(kv_bytes / (att_mean_ms * 1e-3) / 1e9, 1)}
@@ -326,6 +350,7 @@ def main():
                    "variant": args.variant,
                    "kv_dtype": "e4m3" if fp8 else w.dtype,
                    "partition": args.partition if args.variant == "split" else None,
+                   "prefix_plan_ms": round(plan_ms, 4) if plan_ms is not None else None,
                    "accumulate": "f32", "kv_bytes_per_step": kv_bytes,
                    "kv_bytes_unique_per_step": kv_unique},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

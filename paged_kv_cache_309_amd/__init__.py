@@ -20,11 +20,13 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import STATIC_SCRATCH_BYTES, PkvDims, PkvError
+from ._lib import STATIC_SCRATCH_BYTES, PkvDims, PkvError, PkvPrefixInfo
 
 __all__ = ["reshape_and_cache", "paged_attention_decode",
            "paged_attention_decode_split", "split_workspace_bytes",
            "paged_attention_decode_split_static", "STATIC_SCRATCH_BYTES",
+           "PrefixPlan", "paged_attention_decode_shared_prefix",
+           "shared_prefix_workspace_bytes",
            "paged_attention_prefill", "new_kv_cache", "copy_blocks",
            "swap_blocks", "BlockManager", "PkvError", "version"]
 
@@ -277,6 +279,89 @@ def paged_attention_decode_split_static(out: torch.Tensor, q: torch.Tensor,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), float(scale), bs, int(partition_size),
         ctypes.byref(dims), _stream(stream)))
+    return out
+
+
+class PrefixPlan:
+    """The sets of sequences that share leading blocks, found on the host by
+    pkv_prefix_plan from host copies of the block tables and context
+    lengths, with the plan array copied to `device` (the current GPU by
+    default).  `info` holds its sizes; `host` the array itself."""
+
+    def __init__(self, block_tables, context_lens, block_size: int,
+                 min_sharers: int = 2, device=None):
+        import numpy as np
+        bt = np.ascontiguousarray(
+            block_tables.cpu().numpy() if isinstance(block_tables, torch.Tensor)
+            else block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(
+            context_lens.cpu().numpy() if isinstance(context_lens, torch.Tensor)
+            else context_lens, dtype=np.int32)
+        if bt.ndim != 2 or cl.shape != (bt.shape[0],):
+            raise ValueError(f"block_tables {bt.shape} and context_lens {cl.shape} "
+                             "do not describe the same sequences")
+        S, MB = bt.shape
+        plan = np.empty(4 * S + 1, np.int32)
+        self.info = PkvPrefixInfo()
+        _lib.check(_lib.lib().pkv_prefix_plan(
+            bt.ctypes.data, cl.ctypes.data, S, MB, int(block_size),
+            int(min_sharers), plan.ctypes.data, plan.size, ctypes.byref(self.info)))
+        i = self.info
+        self.host = plan[:S + 2 * i.num_groups + 1 + i.num_members].copy()
+        self.block_size = int(block_size)
+        dev = device if device is not None else \
+            torch.device("cuda", torch.cuda.current_device())
+        self.device = torch.from_numpy(self.host).to(dev)
+
+    @property
+    def seq_prefix(self):
+        return self.host[:self.info.num_seqs]
+
+
+def shared_prefix_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, plan: PrefixPlan,
+                                  block_size: int | None = None) -> int:
+    _rank(q, "q", 3)
+    _rank(k_cache, "k_cache", 4)
+    _rank(block_tables, "block_tables", 2)
+    bs = _block_size(block_size, k_cache.shape[2])
+    dims = _dims(q, k_cache, block_tables)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.lib().paged_attention_shared_prefix_workspace_bytes(
+        ctypes.byref(dims), bs, ctypes.byref(plan.info), ctypes.byref(n)))
+    return n.value
+
+
+def paged_attention_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor,
+                                         k_cache: torch.Tensor,
+                                         v_cache: torch.Tensor,
+                                         block_tables: torch.Tensor,
+                                         context_lens: torch.Tensor,
+                                         scale: float, plan: PrefixPlan,
+                                         workspace: torch.Tensor,
+                                         block_size: int | None = None,
+                                         stream=None) -> torch.Tensor:
+    """paged_attention_decode with every sharer set's common prefix computed
+    once for all its members (fp16/bf16): `plan` comes from PrefixPlan over
+    the same tables and lengths; `workspace` is a device byte tensor of at
+    least shared_prefix_workspace_bytes(...)."""
+    dims, bs = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                              context_lens, block_size)
+    if _is_fp8(k_cache):
+        raise ValueError("paged_attention_decode_shared_prefix takes 16-bit caches")
+    if not isinstance(plan, PrefixPlan):
+        raise ValueError("plan must be a PrefixPlan")
+    if plan.block_size != bs or plan.info.num_seqs != q.shape[0]:
+        raise ValueError("the plan was built for another batch or block size")
+    _expect(workspace, "workspace")
+    _on_one_device(out, q, k_cache, v_cache, block_tables, context_lens,
+                   plan.device, workspace, stream=stream)
+    _lib.check(_lib.lib().paged_attention_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), bs, _ptr(plan.device),
+        ctypes.byref(plan.info), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.byref(dims),
+        _stream(stream)))
     return out
 
 

@@ -40,7 +40,9 @@ EXPORTS = ("reshape_and_cache", "paged_attention_decode",
            "pkv_bm_swap_in", "pkv_bm_num_free_host_blocks",
            "pkv_bm_host_refcount", "pkv_bm_is_swapped", "pkv_bm_block_table",
            "paged_attention_prefill", "paged_attention_prefill_fp8",
-           "paged_attention_decode_split_static")
+           "paged_attention_decode_split_static", "pkv_prefix_plan",
+           "paged_attention_shared_prefix_workspace_bytes",
+           "paged_attention_decode_shared_prefix")
 
 
 class PkvDims(ctypes.Structure):
@@ -49,6 +51,12 @@ class PkvDims(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class PkvPrefixInfo(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("num_members", ctypes.c_int32), ("max_members", ctypes.c_int32),
+                ("max_prefix_tokens", ctypes.c_int32)]
 
 
 class PkvError(RuntimeError):
@@ -135,6 +143,15 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_split_static.restype = I
     lib.paged_attention_decode_split_static.argtypes = [P, P, P, P, P, P, F, I,
                                                         I, D, P]
+    PI = ctypes.POINTER(PkvPrefixInfo)
+    lib.pkv_prefix_plan.restype = I
+    lib.pkv_prefix_plan.argtypes = [P, P, I, I, I, I, P, ctypes.c_size_t, PI]
+    lib.paged_attention_shared_prefix_workspace_bytes.restype = I
+    lib.paged_attention_shared_prefix_workspace_bytes.argtypes = [
+        D, I, PI, ctypes.POINTER(ctypes.c_size_t)]
+    lib.paged_attention_decode_shared_prefix.restype = I
+    lib.paged_attention_decode_shared_prefix.argtypes = [
+        P, P, P, P, P, P, F, I, P, PI, P, ctypes.c_size_t, D, P]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_version.restype = I

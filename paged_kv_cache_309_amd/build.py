@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "decode_vector.hip", "decode_mfma.hip",
            "prefill_mfma.hip", "reduce_and_cache.hip", "copy_blocks.hip",
-           "block_manager.cpp"]
+           "block_manager.cpp", "prefix_plan.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

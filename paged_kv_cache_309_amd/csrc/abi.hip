@@ -10,6 +10,7 @@
 #include "pkv.h"
 #include "pkv_blocks.h"
 #include "pkv_internal.h"
+#include "pkv_prefix.h"
 
 namespace {
 
@@ -344,6 +345,101 @@ int decode_split(void *out, const void *q, const void *k_cache, const void *v_ca
   return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+// ---- shared-prefix decode ------------------------------------------------
+// Chunking of the prefixes: enough (set, KV head, chunk) units that the
+// prefix launch fills the chip's 256 compute units once, in chunks of at
+// least 128 tokens (a multiple of the 32-token super-tile).  Fixed by the
+// sizes alone, so that the workspace size is known before any device call.
+constexpr int kPrefixTargetWorkgroups = 256;
+constexpr int kPrefixMinChunk = 128;
+constexpr int kPrefixMaxChunks = 16;  // the vector decode kernel's row states
+constexpr int kPrefixMemberTarget = 256;
+
+struct PrefixChunks {
+  int q_blocks;      // row blocks of the largest set (member blocks of 16
+                     // for multi-head attention)
+  int chunk_tokens;
+  int n_chunks;
+};
+
+// Multi-head attention (one query head per KV head) takes its prefix on
+// the grouped-query decode kernel's structure: 16 members of a set are the
+// columns of the products, the four wavefronts split the whole prefix, and
+// one partial per (member, head) comes out: a few MB where the chunked
+// products would write one per chunk.  Grouped-query attention fills the
+// columns with a member's heads instead, so it takes the chunked products,
+// whose 128-row blocks read each chunk once for 128 / G members.
+bool prefix_by_members(const pkv_dims *d) { return d->num_heads == d->num_kv_heads; }
+
+int prefix_chunks(const pkv_dims *d, const pkv_prefix_info *info, PrefixChunks *pc) {
+  if (prefix_by_members(d)) {
+    // chunks (of at least 256 tokens) only when the (set, head, member
+    // block) units leave compute units idle: each chunk adds a partial per
+    // (member, head), and more workgroups reading one head's tiles slow
+    // each other down (128 members x 32 heads over 1024 tokens: one chunk
+    // 16.6 us, two 17.4, four 22.3, then the decode 91.0 / 91.3 / 92.5 us)
+    pc->q_blocks = (info->max_members + 15) / 16;
+    const int64_t base = (int64_t)info->num_groups * d->num_kv_heads * pc->q_blocks;
+    const int64_t tok = info->max_prefix_tokens;
+    int64_t n = base > 0 ? (kPrefixMemberTarget + base - 1) / base : 1;
+    const int64_t most = (tok + 255) / 256;
+    n = n < most ? n : most;
+    n = n < kPrefixMaxChunks ? n : kPrefixMaxChunks;
+    n = n < 1 ? 1 : n;
+    int64_t ck = (tok + n - 1) / n;
+    ck = (ck + 15) / 16 * 16;
+    ck = ck < 16 ? 16 : ck;
+    pc->chunk_tokens = (int)ck;
+    pc->n_chunks = (int)((tok + ck - 1) / ck);
+    if ((int64_t)info->num_groups * pc->q_blocks * pc->n_chunks > kMaxGridYZ)
+      return PKV_ERR_SHAPE;
+    return PKV_OK;
+  }
+  const int G = d->num_heads / d->num_kv_heads;
+  const int rpw = pkv::prefill_rows_per_workgroup();
+  const int64_t rows = (int64_t)info->max_members * G;
+  pc->q_blocks = (int)((rows + rpw - 1) / rpw);
+  const int64_t base = (int64_t)info->num_groups * d->num_kv_heads * pc->q_blocks;
+  const int64_t tok = info->max_prefix_tokens;
+  int64_t n = base > 0 ? (kPrefixTargetWorkgroups + base - 1) / base : 1;
+  const int64_t most = (tok + kPrefixMinChunk - 1) / kPrefixMinChunk;
+  n = n < most ? n : most;
+  n = n < kPrefixMaxChunks ? n : kPrefixMaxChunks;
+  n = n < 1 ? 1 : n;
+  int64_t ck = (tok + n - 1) / n;
+  ck = (ck + 31) / 32 * 32;
+  if (ck < 32) ck = 32;
+  pc->chunk_tokens = (int)ck;
+  pc->n_chunks = (int)((tok + ck - 1) / ck);
+  if (pkv::prefix_grid(info->num_groups, d->num_kv_heads, pc->n_chunks, pc->q_blocks) >
+      INT_MAX)
+    return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+// The plan's sizes against the dims; fills the chunking and the workspace
+// bytes (0 when no set is planned).
+int check_prefix(const pkv_dims *d, int block_size, const pkv_prefix_info *info,
+                 PrefixChunks *pc, size_t *ws_bytes) {
+  if (!info) return PKV_ERR_NULL;
+  if (info->num_seqs != d->num_seqs || info->num_groups < 0 || info->num_members < 0 ||
+      info->max_members < 0 || info->max_prefix_tokens < 0 ||
+      info->num_members > d->num_seqs || info->max_members > info->num_members ||
+      2 * (int64_t)info->num_groups > info->num_members ||
+      (int64_t)info->max_prefix_tokens > (int64_t)d->max_blocks_per_seq * block_size)
+    return PKV_ERR_SHAPE;
+  *ws_bytes = 0;
+  *pc = PrefixChunks{0, 0, 0};
+  if (info->num_groups == 0 || info->max_prefix_tokens == 0) return PKV_OK;
+  const int rc = prefix_chunks(d, info, pc);
+  if (rc != PKV_OK) return rc;
+  const u128 b = (u128)d->num_seqs * (u128)d->num_heads * (u128)pc->n_chunks *
+                 (u128)(d->head_dim + 2) * 4;
+  if (b > ((u128)1 << 62)) return PKV_ERR_SHAPE;
+  *ws_bytes = (size_t)b;
+  return PKV_OK;
+}
+
 // ---- the allocation-free split decode's scratch ----------------------------
 // For callers that cannot allocate device memory.  The split partials of
 // paged_attention_decode_split_static live in this array; every device the
@@ -494,6 +590,114 @@ int paged_attention_decode_split_static(void *out, const void *q, const void *k_
   return decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                       block_size, partition_size, ws, (size_t)PKV_STATIC_SCRATCH_BYTES, dims,
                       stream, kCacheSame, 1.f, 1.f);
+}
+
+int paged_attention_shared_prefix_workspace_bytes(const pkv_dims *dims, int block_size,
+                                                  const pkv_prefix_info *info,
+                                                  size_t *bytes) {
+  if (!bytes) return PKV_ERR_NULL;
+  size_t qb = 0, cb = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  PrefixChunks pc{};
+  return check_prefix(dims, block_size, info, &pc, bytes);
+}
+
+int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k_cache,
+                                         const void *v_cache, const int32_t *block_tables,
+                                         const int32_t *context_lens, float scale,
+                                         int block_size, const int32_t *prefix_plan,
+                                         const pkv_prefix_info *info, void *workspace,
+                                         size_t workspace_bytes, const pkv_dims *dims,
+                                         pkv_stream_t stream) {
+  size_t qb = 0, cb = 0, need = 0;
+  int rc = check_decode(dims, block_size, &qb, &cb);
+  if (rc != PKV_OK) return rc;
+  if (dims->dtype == PKV_F32) return PKV_ERR_DTYPE;  // the prefix runs on the matrix cores
+  PrefixChunks pc{};
+  rc = check_prefix(dims, block_size, info, &pc, &need);
+  if (rc != PKV_OK) return rc;
+  if (need == 0)  // no shared prefix: the ordinary decode
+    return decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                  dims, stream, kCacheSame, 1.f, 1.f);
+  if (dims->num_seqs == 0) return PKV_OK;
+  rc = check_decode_ptrs(out, q, k_cache, v_cache, block_tables, context_lens, dims, qb, cb);
+  if (rc != PKV_OK) return rc;
+  if (!prefix_plan) return PKV_ERR_NULL;
+  if (!aligned(prefix_plan, 4)) return PKV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  const size_t pb = 4 * ((size_t)dims->num_seqs + 2 * (size_t)info->num_groups + 1 +
+                         (size_t)info->num_members);
+  const size_t tb = (size_t)dims->num_seqs * (size_t)dims->max_blocks_per_seq * 4;
+  const size_t lb = (size_t)dims->num_seqs * 4;
+  if (overlap(out, qb, prefix_plan, pb) || overlap(workspace, need, out, qb) ||
+      overlap(workspace, need, q, qb) || overlap(workspace, need, k_cache, cb) ||
+      overlap(workspace, need, v_cache, cb) || overlap(workspace, need, block_tables, tb) ||
+      overlap(workspace, need, context_lens, lb) || overlap(workspace, need, prefix_plan, pb))
+    return PKV_ERR_ALIAS;
+
+  const size_t n = (size_t)dims->num_seqs * dims->num_heads * pc.n_chunks;
+  float *ws_o = static_cast<float *>(workspace);
+  float *ws_m = ws_o + n * dims->head_dim;
+  float *ws_l = ws_m + n;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+  pkv::PrefillArgs p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.scale_log2 = scale_log2;
+  p.v_scale = 1.f;
+  p.num_seqs = dims->num_seqs;
+  p.num_heads = dims->num_heads;
+  p.num_kv_heads = dims->num_kv_heads;
+  p.num_blocks = dims->num_blocks;
+  p.max_blocks = dims->num_blocks > 0 ? dims->max_blocks_per_seq : 0;
+  p.q_blocks = pc.q_blocks;
+  p.plan = prefix_plan;
+  p.ws_o = ws_o;
+  p.ws_m = ws_m;
+  p.ws_l = ws_l;
+  p.num_groups = info->num_groups;
+  p.num_members = info->num_members;
+  p.chunk_tokens = pc.chunk_tokens;
+  p.n_chunks = pc.n_chunks;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  pkv::DecodeArgs a = make_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                block_size, dims);
+  hipError_t err = hipSuccess;
+  if (prefix_by_members(dims)) {
+    pkv::DecodeArgs b = a;
+    b.plan = prefix_plan;
+    b.num_groups = info->num_groups;
+    b.num_members = info->num_members;
+    b.member_blocks = pc.q_blocks;
+    b.pchunk_tokens = pc.chunk_tokens;
+    b.n_pchunks = pc.n_chunks;
+    b.ws_o = ws_o;
+    b.ws_m = ws_m;
+    b.ws_l = ws_l;
+    err = pkv::launch_prefix_mha(b, dims->dtype, dims->head_dim, block_size, st);
+  } else {
+    err = pkv::launch_prefix_mfma(p, dims->dtype, dims->dtype, dims->head_dim, block_size, st);
+  }
+  if (err != hipSuccess) return PKV_ERR_LAUNCH;
+
+  a.seq_prefix = prefix_plan;  // its first S entries
+  a.pws_o = ws_o;
+  a.pws_m = ws_m;
+  a.pws_l = ws_l;
+  a.pchunk_tokens = pc.chunk_tokens;
+  a.n_pchunks = pc.n_chunks;
+  err = use_mfma(dims)
+            ? pkv::launch_decode_mfma(a, dims->dtype, dims->dtype, dims->head_dim, block_size,
+                                      false, st)
+            : pkv::launch_decode_vector(a, dims->dtype, dims->dtype, dims->head_dim,
+                                        block_size, false, st);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 int copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,

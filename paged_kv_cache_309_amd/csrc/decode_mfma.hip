@@ -57,7 +57,10 @@ __device__ __forceinline__ uint32_t from_other_half(uint32_t old, uint32_t src) 
 }
 
 // QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
-template <int QT, int CT, int D, int BS, bool SPLIT>
+// PFX: the shared-prefix partials of multi-head attention instead (below):
+// the 16 columns are up to 16 members of a sharer set, all with query head
+// g = KV head g, walking the set's prefix.
+template <int QT, int CT, int D, int BS, bool SPLIT, bool PFX = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_mfma_kernel(DecodeArgs a) {
   using Ops = MfmaOps<QT>;
@@ -68,6 +71,7 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int NT = D / 16;          // value n-tiles
   constexpr bool KW = F8 && D == 128; // K loaded as whole rows, then exchanged
 
+  static_assert(!(PFX && SPLIT), "prefix partials run single-pass");
   const int g = blockIdx.x;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
@@ -78,10 +82,33 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ float sm_o[kDecodeWaves][16][D + 4];
   __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
   static_assert(sizeof(sm_o) >= kOrderScratchInts * sizeof(int), "order scratch");
-  const int s = SPLIT ? (int)blockIdx.y
-                      : longest_first_seq<kDecodeThreads>(
-                            a.context_lens, a.num_seqs, a.max_blocks * BS, blockIdx.y,
-                            reinterpret_cast<int *>(&sm_o[0][0][0]));
+  // prefix partials: set gi, its members mcol0 .. mcol0 + ncol - 1 as the
+  // columns; the set's first member's table is walked over its prefix
+  const int32_t *members = nullptr;
+  int mcol0 = 0, ncol = G, ptok_set = 0;
+  int s;
+  int pchunk = 0;  // prefix partials: the chunk of the prefix walked
+  if constexpr (PFX) {
+    pchunk = blockIdx.y % a.n_pchunks;
+    const int gm = blockIdx.y / a.n_pchunks;
+    const int gi = gm / a.member_blocks, mb = gm % a.member_blocks;
+    if (gi >= a.num_groups) return;  // the whole workgroup
+    const int32_t *starts = a.plan + a.num_seqs;
+    const int32_t *gtok = starts + a.num_groups + 1;
+    members = gtok + a.num_groups;
+    const int m0 = min(max(starts[gi], 0), a.num_members);
+    const int m1 = min(max(starts[gi + 1], m0), a.num_members);
+    mcol0 = m0 + mb * 16;
+    if (mcol0 >= m1) return;  // the whole workgroup
+    ncol = min(16, m1 - mcol0);
+    s = min(max(members[m0], 0), a.num_seqs - 1);
+    ptok_set = max(0, min(gtok[gi], a.max_blocks * BS));
+  } else {
+    s = SPLIT ? (int)blockIdx.y
+              : longest_first_seq<kDecodeThreads>(a.context_lens, a.num_seqs,
+                                                  a.max_blocks * BS, blockIdx.y,
+                                                  reinterpret_cast<int *>(&sm_o[0][0][0]));
+  }
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
   // split: this wave's partition (the split path has no workgroup barrier,
@@ -89,13 +116,43 @@ decode_mfma_kernel(DecodeArgs a) {
   const int part = SPLIT ? (int)blockIdx.z * kDecodeWaves + w : 0;
   if (SPLIT && part >= a.num_parts) return;
 
-  int L = a.context_lens[s];
+  int L = PFX ? ptok_set : a.context_lens[s];
   L = max(0, min(L, a.max_blocks * BS));
-  const int tok_begin = SPLIT ? part * a.part_tokens : 0;
-  const int tok_end = SPLIT ? min(L, tok_begin + a.part_tokens) : L;
+  // shared-prefix decode: the prefix kernel computed tokens [0, ptok) in
+  // n_pre chunks; the walk starts after them (ptok is a multiple of the
+  // block size, so of the 16-token tile)
+  int ptok = 0, n_pre = 0;
+  if (!SPLIT && !PFX && a.seq_prefix) {
+    ptok = max(0, min(a.seq_prefix[s], L)) & ~15;
+    n_pre = min(a.n_pchunks, (ptok + a.pchunk_tokens - 1) / a.pchunk_tokens);
+  }
+  const int tok_begin = SPLIT ? part * a.part_tokens : PFX ? pchunk * a.pchunk_tokens : ptok;
+  const int tok_end = SPLIT || PFX ? min(L, tok_begin + (SPLIT ? a.part_tokens : a.pchunk_tokens))
+                                   : L;
 
-  if (tok_begin >= tok_end) {
-    if (!SPLIT) {
+  // the (sequence, query head) of column c: head g*G + c of sequence s, or
+  // (prefix partials) head g of member mcol0 + c
+  auto col_row = [&](int c) -> size_t {
+    if constexpr (PFX)
+      return (size_t)min(max(members[mcol0 + c], 0), a.num_seqs - 1) * Hq + g;
+    else
+      return (size_t)s * Hq + g * G + c;
+  };
+  // prefix partials: the partial of column c's (member, head) for this chunk
+  auto pidx = [&](int c) -> size_t { return col_row(c) * a.n_pchunks + pchunk; };
+
+  if (tok_begin >= tok_end && n_pre == 0) {
+    if constexpr (PFX) {
+      // an empty prefix: partials of weight 0
+      for (int i = tid; i < ncol * D; i += kDecodeThreads) {
+        const size_t pi = pidx(i / D);
+        a.ws_o[pi * D + i % D] = 0.f;
+        if (i % D == 0) {
+          a.ws_m[pi] = -INFINITY;
+          a.ws_l[pi] = 0.f;
+        }
+      }
+    } else if (!SPLIT) {
       for (int i = tid; i < G * D; i += kDecodeThreads)
         store_elem<QT>(a.out, ((size_t)s * Hq + g * G) * D + i, 0.f);
     }
@@ -107,12 +164,12 @@ decode_mfma_kernel(DecodeArgs a) {
   // 32*grp + 8*kk (D = 128) or 16*grp + 8*kk (D = 64) for 8-bit caches
   u32x4 qop[KC];
   {
-    const char *qp = static_cast<const char *>(a.q) + ((size_t)s * Hq + g * G + col) * D * 2;
+    const char *qp = static_cast<const char *>(a.q) + col_row(col < ncol ? col : 0) * D * 2;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       const int d0 = F8 ? (KW ? 32 : 16) * grp + 8 * kk : (kk * 4 + grp) * 8;
-      qop[kk] = col < G ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
-                        : u32x4{0u, 0u, 0u, 0u};
+      qop[kk] = col < ncol ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
+                           : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -165,13 +222,18 @@ decode_mfma_kernel(DecodeArgs a) {
 
 
 
+  // tiles are streamed (non-temporal loads); prefix partials read each tile
+  // once per block of 16 members, all on one XCD, so there the loads keep
+  // the lines in its L2
   auto load = [&](Tl &t, size_t tile_bytes) {
     const char *kp = kc + tile_bytes + koff;
     const char *vp = vc + tile_bytes + voff;
 #pragma unroll
-    for (int c = 0; c < Tl::NC; ++c) t.k[c] = load_stream16(kp + c * KSTEP);
+    for (int c = 0; c < Tl::NC; ++c)
+      t.k[c] = PFX ? load_keep16(kp + c * KSTEP) : load_stream16(kp + c * KSTEP);
 #pragma unroll
-    for (int c = 0; c < Tl::NC; ++c) t.v[c] = load_stream16(vp + c * 256);
+    for (int c = 0; c < Tl::NC; ++c)
+      t.v[c] = PFX ? load_keep16(vp + c * 256) : load_stream16(vp + c * 256);
   };
 
   auto compute = [&](Tl &t, int n) {
@@ -206,7 +268,7 @@ decode_mfma_kernel(DecodeArgs a) {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sc[i] = (i < nvalid && col < G) ? sacc[i] * a.scale_log2 : -INFINITY;
+      sc[i] = (i < nvalid && col < ncol) ? sacc[i] * a.scale_log2 : -INFINITY;
     if (tail) {
       // masked tokens' values may hold anything (NaN included): zero them
       if constexpr (F8) {
@@ -265,6 +327,21 @@ decode_mfma_kernel(DecodeArgs a) {
           acc[4 * u + j] = Ops::pv(va, pr, acc[4 * u + j]);
         }
       }
+    } else if constexpr (PFX) {
+      // prefix partials: one probability operand rounded to the 16-bit
+      // type, the sum over exactly the rounded weights (the precision of
+      // the chunked-prefill products); half the value products
+      float r0, r1, r2, r3;
+      const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
+      l += (r0 + r1) + (r2 + r3);
+#pragma unroll
+      for (int u = 0; u < Tl::NC; ++u) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
+          acc[2 * u + j] = Ops::pv(va, pr, acc[2 * u + j]);
+        }
+      }
     } else {
       l += (p[0] + p[1]) + (p[2] + p[3]);
       uint32_t h01, l01, h23, l23;
@@ -289,14 +366,15 @@ decode_mfma_kernel(DecodeArgs a) {
   // tiles of 8-bit caches, two of the 4 KiB 16-bit tiles (measured: 8-bit
   // gqa70b 165 -> 154 us from one to three, 16-bit 278 -> 271 us from one
   // to two)
-  if (n_mine > 0 && F8)
+  if (n_mine > 0 && F8) {
     walk_tiles_n<Tl, 4, kStride>(trow, tile0, n_mine, BS / 16, (unsigned)a.num_blocks,
                         (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
                         load, compute);
-  else if (n_mine > 0)
+  } else if (n_mine > 0) {
     walk_tiles_n<Tl, 3, kStride>(trow, tile0, n_mine, BS / 16, (unsigned)a.num_blocks,
                         (size_t)g * BS * D * E, (size_t)Hkv * BS * D * E, (size_t)16 * D * E,
                         load, compute);
+  }
 
   stage_state();
   if constexpr (SPLIT) {
@@ -319,19 +397,53 @@ decode_mfma_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- merge the 4 wavefronts through LDS ----
+  if constexpr (PFX) {
+    // ---- merge the 4 wavefronts into each member's partial: maximum,
+    //      sum of weights and un-normalised weighted values ----
+    __syncthreads();
+    for (int idx = tid; idx < ncol * D; idx += kDecodeThreads) {
+      const int hh = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kDecodeWaves; ++i) M = fmaxf(M, sm_m[i][hh]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDecodeWaves; ++i) {
+        const float f = fast_exp2(sm_m[i][hh] - M);  // a wave that saw no token: 0
+        num = fmaf(f, sm_o[i][hh][d], num);
+        den = fmaf(f, sm_l[i][hh], den);
+      }
+      const size_t pi = pidx(hh);
+      a.ws_o[pi * D + d] = num;
+      if (d == 0) {
+        a.ws_m[pi] = M;
+        a.ws_l[pi] = den;
+      }
+    }
+    return;
+  }
+
+  // ---- merge the 4 wavefronts through LDS (and the prefix chunks'
+  //      partial states, if any) ----
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
     const int hh = idx / D, d = idx % D;
+    const size_t pbase = ((size_t)s * Hq + g * G + hh) * (size_t)a.n_pchunks;
     float M = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kDecodeWaves; ++i) M = fmaxf(M, sm_m[i][hh]);
+    for (int c = 0; c < n_pre; ++c) M = fmaxf(M, a.pws_m[pbase + c]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int i = 0; i < kDecodeWaves; ++i) {
-      const float f = fast_exp2(sm_m[i][hh] - M);
+      const float f = fast_exp2(sm_m[i][hh] - M);  // a wave that saw no token: m = -inf
       num = fmaf(f, sm_o[i][hh][d], num);
       den = fmaf(f, sm_l[i][hh], den);
+    }
+    for (int c = 0; c < n_pre; ++c) {
+      const float f = fast_exp2(a.pws_m[pbase + c] - M);
+      num = fmaf(f, a.pws_o[(pbase + c) * D + d], num);
+      den = fmaf(f, a.pws_l[pbase + c], den);
     }
     const int h = g * G + hh;
     num *= a.v_scale;  // value dequantisation (1 for 16-bit caches)
@@ -352,6 +464,33 @@ static hipError_t launch_mfma(const DecodeArgs &a, bool split, hipStream_t st) {
   hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, D, BS, false>),
                      dim3(a.num_kv_heads, a.num_seqs, 1), dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int QT, int D, int BS>
+static hipError_t launch_pfx(const DecodeArgs &a, hipStream_t st) {
+  // x = head: all workgroups of one head have ids of one residue mod 8, so
+  // they run on one XCD and re-read the head's prefix from its L2
+  const dim3 grid(a.num_kv_heads, a.num_groups * a.member_blocks * a.n_pchunks, 1);
+  hipLaunchKernelGGL((decode_mfma_kernel<QT, QT, D, BS, false, true>), grid,
+                     dim3(kDecodeThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_mha(const DecodeArgs &a, int dtype, int head_dim, int block_size,
+                             hipStream_t st) {
+  if (a.num_groups == 0 || a.member_blocks == 0) return hipSuccess;
+  if (dtype == DT_F16) {
+    if (head_dim == 128)
+      return block_size == 16 ? launch_pfx<DT_F16, 128, 16>(a, st)
+                              : launch_pfx<DT_F16, 128, 32>(a, st);
+    return block_size == 16 ? launch_pfx<DT_F16, 64, 16>(a, st)
+                            : launch_pfx<DT_F16, 64, 32>(a, st);
+  }
+  if (head_dim == 128)
+    return block_size == 16 ? launch_pfx<DT_BF16, 128, 16>(a, st)
+                            : launch_pfx<DT_BF16, 128, 32>(a, st);
+  return block_size == 16 ? launch_pfx<DT_BF16, 64, 16>(a, st)
+                          : launch_pfx<DT_BF16, 64, 32>(a, st);
 }
 
 template <int QT, int CT>

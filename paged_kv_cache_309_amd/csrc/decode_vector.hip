@@ -131,11 +131,20 @@ decode_vector_kernel(DecodeArgs a) {
     const int C = a.query_start_loc[s + 1] - q0;
     L = max(0, min(L, L - C + (qrow - q0) + 1));
   }
-  const int tok_begin = SPLIT ? part0 * a.part_tokens : 0;
+  // shared-prefix decode: the prefix kernel computed tokens [0, ptok) in
+  // n_pre chunks; the walk starts after them (ptok is a multiple of the
+  // block size, so of the 16-token tile)
+  int ptok = 0, n_pre = 0;
+  if (!SPLIT && !MQ && a.seq_prefix) {
+    ptok = max(0, min(a.seq_prefix[s], L)) & ~15;
+    // at most one chunk per row state (the library plans at most 16 chunks)
+    n_pre = min(min(a.n_pchunks, 16), (ptok + a.pchunk_tokens - 1) / a.pchunk_tokens);
+  }
+  const int tok_begin = SPLIT ? part0 * a.part_tokens : ptok;
   const int tok_end = SPLIT ? min(L, min(a.num_parts, part0 + ppw) * a.part_tokens) : L;
   const size_t orow = ((size_t)(MQ ? qrow : s) * Hq + h) * D;
 
-  if (tok_begin >= tok_end) {
+  if (tok_begin >= tok_end && n_pre == 0) {
     if (!SPLIT) {
       for (int d = tid; d < D; d += kDecodeThreads) store_elem<QT>(a.out, orow + d, 0.f);
     }
@@ -180,6 +189,23 @@ decode_vector_kernel(DecodeArgs a) {
   float acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
+  if (n_pre > 0) {
+    // shared-prefix decode: row state 4w + r starts as the partial state of
+    // prefix chunk 4w + r, so the final merge takes the prefix in with the
+    // rest, and these loads overlap the first tiles' instead of trailing
+    // the walk
+    const int si = w * 4 + r;
+    if (si < n_pre) {
+      const size_t pc = ((size_t)s * Hq + h) * a.n_pchunks + si;
+      m = a.pws_m[pc];
+      l = a.pws_l[pc];
+#pragma unroll
+      for (int ii = 0; ii < Tl::VI; ++ii)
+#pragma unroll
+        for (int k2 = 0; k2 < Tl::DPV; ++k2)
+          acc[ii * Tl::DPV + k2] = a.pws_o[pc * D + (ii * 256 + c * 16) / (4 * E) + k2];
+    }
+  }
 
   // one tile's loads: non-temporal (streamed), or plain for a block the
   // neighbouring sequence shares, which the other sharers read too
@@ -317,10 +343,13 @@ decode_vector_kernel(DecodeArgs a) {
   };
 
   if (n_mine > 0) {
-    // tiles of a prefix the neighbouring sequence shares
+    // tiles of a prefix the neighbouring sequence shares (none to look for
+    // when the prefix kernel took the shared prefix)
     const int shared_tiles =
-        shared_prefix_blocks<BS>(a.block_tables, a.max_blocks, a.num_seqs, s, tok_end, lane) *
-        (BS / 16);
+        a.seq_prefix ? 0
+                     : shared_prefix_blocks<BS>(a.block_tables, a.max_blocks, a.num_seqs, s,
+                                                tok_end, lane) *
+                           (BS / 16);
     // the wave's tiles in front of shared_tiles are read with plain loads,
     // the rest streamed; two walks, each with its own exact waits
     const int n_keep =

@@ -68,6 +68,26 @@ struct DecodeArgs {
   // nullptr for decode.
   const int32_t *query_start_loc;
   int num_query_tokens;
+  // shared-prefix decode (single pass): tokens [0, seq_prefix[s]) of
+  // sequence s were computed by the prefix kernel, which left the partial
+  // states of its chunks of pchunk_tokens tokens in pws_* ([S, Hq,
+  // n_pchunks, D] weighted sums, [S, Hq, n_pchunks] maxima in log2 units
+  // and sums); the walk starts after them and the final merge takes them
+  // in.  nullptr otherwise.
+  const int32_t *seq_prefix;
+  const float *pws_o;
+  const float *pws_m;
+  const float *pws_l;
+  int pchunk_tokens;
+  int n_pchunks;
+  // shared-prefix partials on the grouped-query kernel's structure (one
+  // KV head per query head): the plan of pkv_prefix_plan, its set count,
+  // member count and member blocks of 16 per set; the partials go to ws_*
+  // ([S, Hq] rows, one chunk covering the whole prefix)
+  const int32_t *plan;
+  int num_groups;
+  int num_members;
+  int member_blocks;
 };
 
 struct CacheWriteArgs {
@@ -116,6 +136,18 @@ struct PrefillArgs {
   int max_blocks;
   int num_query_tokens;
   int q_blocks;      // grid extent over the query rows of one (seq, KV head)
+  // shared-prefix partials (prefix mode): the plan of pkv_prefix_plan, the
+  // partial states of every (member, head, chunk) and the chunking of the
+  // prefixes.  q_blocks is then the grid extent over the rows of one (set,
+  // KV head, chunk).
+  const int32_t *plan;
+  float *ws_o;       // [S, Hq, n_chunks, D]
+  float *ws_m;       // [S, Hq, n_chunks], log2 units
+  float *ws_l;       // [S, Hq, n_chunks]
+  int num_groups;
+  int num_members;
+  int chunk_tokens;  // a multiple of 32
+  int n_chunks;
 };
 
 // Each returns the launch error (hipSuccess when enqueued).
@@ -142,6 +174,18 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
 // number of workgroups a prefill launch takes
 int prefill_rows_per_workgroup();
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int q_blocks);
+// Shared-prefix partials: every (set, KV head, chunk) of the plan, its
+// member rows times the group's query heads in row blocks of
+// prefill_rows_per_workgroup(); workgroups a launch takes.
+hipError_t launch_prefix_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
+                              int head_dim, int block_size, hipStream_t st);
+// Shared-prefix partials for multi-head attention: one workgroup per
+// (KV head, set, block of 16 members) walks the whole prefix, its four
+// wavefronts splitting the tiles, and writes one partial per (member,
+// head).
+hipError_t launch_prefix_mha(const DecodeArgs &a, int dtype, int head_dim,
+                             int block_size, hipStream_t st);
+int64_t prefix_grid(int num_groups, int num_kv_heads, int n_chunks, int q_blocks);
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, int num_pairs,
                               hipStream_t st);
 

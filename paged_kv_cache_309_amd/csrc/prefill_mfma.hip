@@ -58,6 +58,8 @@
 // it adds exactly the rounded weights the value product applied, and the
 // softmax stays off the vector ALUs as far as possible: per logit one fused
 // multiply-add and one exp2, plus the running maximum.  Accumulation is fp32.
+#include <limits.h>
+
 #include <type_traits>
 
 #include "mfma_ops.h"
@@ -125,8 +127,9 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
 }
 
-// QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
-template <int QT, int CT, int D, int BS>
+// QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3).
+// PREFIX: the shared-prefix partials instead of chunked prefill (below).
+template <int QT, int CT, int D, int BS, bool PREFIX = false>
 __global__ void __launch_bounds__(kPrefillThreads)
 prefill_mfma_kernel(PrefillArgs a) {
   using Ops = MfmaOps<QT>;
@@ -146,56 +149,117 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int wgi = blockIdx.x;
   const int xcd = wgi % kXcds, nth = wgi / kXcds;
   const int pair = (nth / a.q_blocks) * kXcds + xcd;
-  if (pair >= a.num_seqs * Hkv) return;  // the whole workgroup
   const int blk = a.q_blocks - 1 - nth % a.q_blocks;
-  const int s = pair / Hkv, g = pair % Hkv;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
 
-  const int T = a.num_query_tokens;
-  const int q0 = min(max(a.query_start_loc[s], 0), T);
-  const int q1 = min(max(a.query_start_loc[s + 1], q0), T);
-  const int C = q1 - q0;
-  const int L = max(0, min(a.context_lens[s], a.max_blocks * BS));
-  const int R = C * G;
-  const int wg_row0 = blk * kPrefillRows;
-  if (wg_row0 >= R) return;  // the whole workgroup
-  const int wg_row_last = min(wg_row0 + kPrefillRows, R) - 1;
-  const int wg_kv_end = min(L, L - C + wg_row_last / G + 1);
-  const int n_super = wg_kv_end > 0 ? (wg_kv_end + 31) >> 5 : 0;
-
-  // this wavefront's rows
-  const int row0 = wg_row0 + w * NQ * 16;
-  const bool has_rows = row0 <= wg_row_last;
-  const int row_last = min(row0 + NQ * 16 - 1, wg_row_last);
-  const int pos_first = L - C + row0 / G;  // rows ascend with positions
-  const int kv_end_w = has_rows ? min(L, L - C + row_last / G + 1) : 0;
-  const int n_super_w = kv_end_w > 0 ? (kv_end_w + 31) >> 5 : 0;
-
+  // The walk covers tokens kv0 .. kv0 + L - 1 of sequence s's block table
+  // (token offsets inside the walk are relative to kv0); n_super super-tiles
+  // for the workgroup, n_super_w of them computed by this wavefront, whose
+  // rows are row0 .. row_last.
+  int s, g, L, kv0 = 0, n_super, n_super_w, row0, row_last, pos_first;
   int pos[NQ];
-  size_t orow[NQ];
+  size_t orow[NQ];   // q row (and, prefill, out row) of each row tile
+  size_t pidx[NQ];   // prefix mode: the partial of each row tile
+  // prefix mode: rows of one (set, KV head, chunk) are the set's members
+  // times the G query heads of the group, row r = member r / G, head r % G;
+  // they all attend to every token of the chunk, which the set's first
+  // member's table maps (all members map the same blocks there)
+  const int32_t *members = nullptr;
+  int m0 = 0, chunk = 0;
+  if constexpr (PREFIX) {
+    if (pair >= a.num_groups * Hkv * a.n_chunks) return;  // the whole workgroup
+    chunk = pair % a.n_chunks;
+    g = (pair / a.n_chunks) % Hkv;
+    const int gi = pair / a.n_chunks / Hkv;
+    const int32_t *starts = a.plan + a.num_seqs;
+    const int32_t *gtok = starts + a.num_groups + 1;
+    members = gtok + a.num_groups;
+    m0 = min(max(starts[gi], 0), a.num_members);
+    const int m1 = min(max(starts[gi + 1], m0), a.num_members);
+    const int R = (m1 - m0) * G;
+    const int wg_row0 = blk * kPrefillRows;
+    if (wg_row0 >= R) return;  // the whole workgroup
+    s = min(max(members[m0], 0), a.num_seqs - 1);
+    // the set's prefix lies inside every member's context (the planner
+    // guarantees it), and inside the table whatever the plan holds
+    const int ptok = max(0, min(gtok[gi], a.max_blocks * BS));
+    kv0 = chunk * a.chunk_tokens;
+    if (kv0 >= ptok) return;  // the whole workgroup
+    L = min(a.chunk_tokens, ptok - kv0);
+    n_super = (L + 31) >> 5;
+    const int wg_row_last = min(wg_row0 + kPrefillRows, R) - 1;
+    row0 = wg_row0 + w * NQ * 16;
+    row_last = min(row0 + NQ * 16 - 1, wg_row_last);
+    n_super_w = row0 <= wg_row_last ? n_super : 0;
+    pos_first = INT_MAX;  // no causal mask
+  } else {
+    if (pair >= a.num_seqs * Hkv) return;  // the whole workgroup
+    s = pair / Hkv;
+    g = pair % Hkv;
+  }
+  const int T = a.num_query_tokens;
+  const int q0 = PREFIX ? 0 : min(max(a.query_start_loc[s], 0), T);
+  const int q1 = PREFIX ? 0 : min(max(a.query_start_loc[s + 1], q0), T);
+  const int C = q1 - q0;
+  if constexpr (!PREFIX) {
+    L = max(0, min(a.context_lens[s], a.max_blocks * BS));
+    const int R = C * G;
+    const int wg_row0 = blk * kPrefillRows;
+    if (wg_row0 >= R) return;  // the whole workgroup
+    const int wg_row_last = min(wg_row0 + kPrefillRows, R) - 1;
+    const int wg_kv_end = min(L, L - C + wg_row_last / G + 1);
+    n_super = wg_kv_end > 0 ? (wg_kv_end + 31) >> 5 : 0;
+
+    // this wavefront's rows
+    row0 = wg_row0 + w * NQ * 16;
+    const bool has_rows = row0 <= wg_row_last;
+    row_last = min(row0 + NQ * 16 - 1, wg_row_last);
+    pos_first = L - C + row0 / G;  // rows ascend with positions
+    const int kv_end_w = has_rows ? min(L, L - C + row_last / G + 1) : 0;
+    n_super_w = kv_end_w > 0 ? (kv_end_w + 31) >> 5 : 0;
+  }
+
   u32x4 qop[NQ][KC];
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const int r = row0 + qt * 16 + col;
     const bool valid = r <= row_last;
     const int j = valid ? r / G : 0, hh = valid ? r % G : 0;
-    pos[qt] = valid ? L - C + j : -1;
-    orow[qt] = ((size_t)(q0 + j) * Hq + g * G + hh) * D;
-    const char *qp = static_cast<const char *>(a.q) + orow[qt] * 2;
-    // the eight dims logit product kk takes from this lane: chunk kk*4+grp
-    // of the row (16-bit caches); half kk%2 of the 16 dims of 8-bit chunk
-    // (kk/2)*4+grp
-#pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      const int off = F8 ? 32 * ((kk / 2) * 4 + grp) + 16 * (kk % 2) : (kk * 4 + grp) * 16;
-      qop[qt][kk] = valid ? *reinterpret_cast<const u32x4 *>(qp + off) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (PREFIX) {
+      const int sq = valid ? min(max(members[m0 + j], 0), a.num_seqs - 1) : 0;
+      pos[qt] = valid ? INT_MAX : -1;
+      orow[qt] = ((size_t)sq * Hq + g * G + hh) * D;
+      pidx[qt] = ((size_t)sq * Hq + g * G + hh) * a.n_chunks + chunk;
+    } else {
+      pos[qt] = valid ? L - C + j : -1;
+      orow[qt] = ((size_t)(q0 + j) * Hq + g * G + hh) * D;
+      pidx[qt] = 0;
     }
   }
-  // the queries are in registers before the ring's loads are counted
-  wait_vm<0>();
+  // the eight dims logit product kk takes from this lane: chunk kk*4+grp of
+  // the row (16-bit caches); half kk%2 of the 16 dims of 8-bit chunk
+  // (kk/2)*4+grp
+  auto load_q = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      const bool valid = row0 + qt * 16 + col <= row_last;
+      const char *qp = static_cast<const char *>(a.q) + orow[qt] * 2;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        const int off = F8 ? 32 * ((kk / 2) * 4 + grp) + 16 * (kk % 2) : (kk * 4 + grp) * 16;
+        qop[qt][kk] =
+            valid ? *reinterpret_cast<const u32x4 *>(qp + off) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  if constexpr (!PREFIX) {
+    load_q();
+    // the queries are in registers before the ring's loads are counted
+    wait_vm<0>();
+  }
 
   // block-table entries are wave-uniform: read through the scalar cache
   const __attribute__((address_space(4))) int32_t *trow =
@@ -220,7 +284,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   // the context: any block, its contents are masked)
   auto lookup = [&](int n) -> int {
     const unsigned tb = 32u * n + 16u * (w & 1);
-    const int phys = tb < (unsigned)L ? trow[tb / BS] : 0;
+    const int phys = tb < (unsigned)L ? trow[(kv0 + tb) / BS] : 0;
     return (unsigned)phys < (unsigned)a.num_blocks ? phys : 0;
   };
   // wavefront w fills piece w of super-tile n into stage n % S
@@ -229,7 +293,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     // phys is in [0, num_blocks) and a block is far below 4 GiB: an unsigned
     // 32 x 32 -> 64-bit product
     const char *src = src_base + (uint64_t)(unsigned)phys * (unsigned)block_bytes +
-                      (tb % BS) * D * E;
+                      ((kv0 + tb) % BS) * D * E;
     char *dst = ring + stage * RG::TILE + w * RG::PIECE;
 #pragma unroll
     for (int b = 0; b < RG::LOADS; ++b)
@@ -271,7 +335,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   auto compute = [&](int n, int stage, auto may_tail) {
     constexpr bool MAY_TAIL = decltype(may_tail)::value;
     const char *base = ring + stage * RG::TILE;
-    const bool diag = 32 * n + 31 > pos_first;
+    const bool diag = !PREFIX && 32 * n + 31 > pos_first;
     // K operands of both tiles first: the logit products wait only for them,
     // and the value reads complete while those products run
     u32x4 kop[2][KC];
@@ -352,10 +416,20 @@ prefill_mfma_kernel(PrefillArgs a) {
         }
     }
     if (MAY_TAIL && 32 * n + 32 > L) {
-      // tokens at or past L may hold anything (NaN included): zero their values
+      // tokens at or past L may hold anything (NaN included): zero their
+      // values.  Their logits are masked too: by the causal mask in prefill
+      // (every row's position is below L), here in prefix mode, which has
+      // none.
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int nvalid = max(0, min(4, L - (32 * n + 16 * st + 4 * grp)));
+        if constexpr (PREFIX) {
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i >= nvalid) x[qt][st][i] = -INFINITY;
+        }
         if constexpr (F8) {
           const uint32_t mk = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
 #pragma unroll
@@ -437,6 +511,14 @@ prefill_mfma_kernel(PrefillArgs a) {
   static_assert((S - 2) * RG::LOADS < 16, "vmcnt range");
   const int n_pre = min(S - 1, n_super);
   for (int n = 0; n < n_pre; ++n) issue(n, lookup(n), n);
+  if constexpr (PREFIX) {
+    // a chunk is a few super-tiles: the queries load together with the
+    // first ones (one latency instead of two), and all of them are waited
+    // for before the first step, after which only the ring's loads are
+    // outstanding and the counts below are exact again
+    load_q();
+    wait_vm<0>();
+  }
   // the table entry of the next super-tile to issue is read one iteration
   // ahead, so its latency hides behind a compute and a barrier
   int phys_next = n_pre < n_super ? lookup(n_pre) : 0;
@@ -475,6 +557,44 @@ prefill_mfma_kernel(PrefillArgs a) {
   }
   static_assert(S == 4, "the general loop's waits cover S - 2 = 2 later super-tiles");
 
+  if constexpr (PREFIX) {
+    // the partial state of each row: maximum (log2 units), sum of the
+    // weights and weighted sum of values, un-normalised; every row of a
+    // chunk saw at least one token, so its maximum is finite.  Row m =
+    // 4*grp + i of n-tile 2u+j is dim 32u + 2m + j (16-bit caches; two
+    // adjacent dims stored together), of n-tile 4u+j dim 64u + 4m + j
+    // (8-bit caches; four adjacent dims stored together).
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      if (row0 + qt * 16 + col > row_last) continue;  // no row in this column
+      float *po = a.ws_o + pidx[qt] * D;
+      if (grp == 0) {
+        a.ws_m[pidx[qt]] = m[qt];
+        a.ws_l[pidx[qt]] = lsum[qt][0];
+      }
+      if constexpr (F8) {
+#pragma unroll
+        for (int u = 0; u < V8; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4 *>(po + 64 * u + 4 * (4 * grp + i)) =
+                f32x4{acc[qt][4 * u][i], acc[qt][4 * u + 1][i], acc[qt][4 * u + 2][i],
+                      acc[qt][4 * u + 3][i]};
+      } else {
+        // dims 32u + 8*grp .. +7 of the row are this lane's (i, j) = (0, 0),
+        // (0, 1), (1, 0), ...: two 16-byte stores
+#pragma unroll
+        for (int u = 0; u < NC; ++u)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            *reinterpret_cast<f32x4 *>(po + 32 * u + 8 * grp + 4 * hf) =
+                f32x4{acc[qt][2 * u][2 * hf], acc[qt][2 * u + 1][2 * hf],
+                      acc[qt][2 * u][2 * hf + 1], acc[qt][2 * u + 1][2 * hf + 1]};
+      }
+    }
+    return;
+  }
+
   // normalise and store: row m = 4*grp + i of n-tile 2u+j is dim
   // 32u + 2m + j of the lane's query row (16-bit caches; two adjacent dims
   // stored as one 32-bit word), of n-tile 4u+j dim 64u + 4m + j (8-bit
@@ -509,6 +629,37 @@ prefill_mfma_kernel(PrefillArgs a) {
       }
     }
   }
+}
+
+int64_t prefix_grid(int num_groups, int num_kv_heads, int n_chunks, int q_blocks) {
+  const int64_t units = (int64_t)num_groups * num_kv_heads * n_chunks;
+  return (int64_t)kXcds * ((units + kXcds - 1) / kXcds) * q_blocks;
+}
+
+template <int QT, int CT, int D, int BS>
+static hipError_t launch_prefix(const PrefillArgs &a, hipStream_t st) {
+  const int64_t n = prefix_grid(a.num_groups, a.num_kv_heads, a.n_chunks, a.q_blocks);
+  hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, true>), dim3((unsigned)n),
+                     dim3(kPrefillThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int QT, int CT>
+static hipError_t launch_prefix_dt(const PrefillArgs &a, int head_dim, int block_size,
+                                   hipStream_t st) {
+  if (head_dim == 128)
+    return block_size == 16 ? launch_prefix<QT, CT, 128, 16>(a, st)
+                            : launch_prefix<QT, CT, 128, 32>(a, st);
+  return block_size == 16 ? launch_prefix<QT, CT, 64, 16>(a, st)
+                          : launch_prefix<QT, CT, 64, 32>(a, st);
+}
+
+hipError_t launch_prefix_mfma(const PrefillArgs &a, int dtype, int cache_dtype, int head_dim,
+                              int block_size, hipStream_t st) {
+  if (a.num_groups == 0 || a.q_blocks == 0 || a.n_chunks == 0) return hipSuccess;
+  (void)cache_dtype;  // 16-bit caches of the query's type
+  if (dtype == DT_F16) return launch_prefix_dt<DT_F16, DT_F16>(a, head_dim, block_size, st);
+  return launch_prefix_dt<DT_BF16, DT_BF16>(a, head_dim, block_size, st);
 }
 
 template <int QT, int CT, int D, int BS>

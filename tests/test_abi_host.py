@@ -377,3 +377,49 @@ def test_python_binding_checks_shapes_and_dtypes_before_any_launch():
     # well-formed host tensors reach the device check
     with pytest.raises(ValueError, match="CUDA tensors"):
         dec()
+
+
+def test_shared_prefix_checks_before_any_hip_call():
+    """The shared-prefix decode validates the plan's sizes, the workspace and
+    the pointers before any HIP call."""
+    lib = _lib.lib()
+    PLAN = 0x80000000
+
+    def info(S_=4, G=1, M=3, maxm=3, tok=64):
+        return _lib.PkvPrefixInfo(S_, G, M, maxm, tok)
+
+    def sp(d, inf, bs=16, out=A, q=B, plan=PLAN, ws=W, wsb=1 << 30):
+        return lib.paged_attention_decode_shared_prefix(
+            out, q, C, DQ, E, F, 0.1, bs, plan,
+            ctypes.byref(inf) if inf is not None else None, ws, wsb,
+            ctypes.byref(d), None)
+
+    def need(d, inf, bs=16):
+        n = ctypes.c_size_t(0)
+        rc = lib.paged_attention_shared_prefix_workspace_bytes(
+            ctypes.byref(d), bs, ctypes.byref(inf), ctypes.byref(n))
+        return rc, n.value
+    d = dims()   # 4 sequences, 8 query / 2 KV heads, D 128, 8 blocks each
+    # one chunk of the 64-token prefix: 4 * 8 * 1 * (128 + 2) floats
+    assert need(d, info()) == (0, 4 * 8 * 1 * 130 * 4)
+    assert need(d, info(G=0, M=0, maxm=0, tok=0)) == (0, 0)
+    assert sp(dims(dt=0), info()) == ERR["PKV_ERR_DTYPE"]
+    assert sp(d, None) == ERR["PKV_ERR_NULL"]
+    assert sp(d, info(S_=5)) == ERR["PKV_ERR_SHAPE"]
+    assert sp(d, info(G=2, M=3)) == ERR["PKV_ERR_SHAPE"]      # a set of one
+    assert sp(d, info(M=5, maxm=5)) == ERR["PKV_ERR_SHAPE"]   # more members than seqs
+    assert sp(d, info(tok=8 * 16 + 16)) == ERR["PKV_ERR_SHAPE"]
+    assert sp(d, info(maxm=4)) == ERR["PKV_ERR_SHAPE"]
+    assert sp(d, info(), bs=8) == ERR["PKV_ERR_BLOCK_SIZE"]
+    assert sp(d, info(), plan=None) == ERR["PKV_ERR_NULL"]
+    assert sp(d, info(), plan=PLAN + 2) == ERR["PKV_ERR_ALIGN"]
+    assert sp(d, info(), out=None) == ERR["PKV_ERR_NULL"]
+    assert sp(d, info(), wsb=need(d, info())[1] - 1) == ERR["PKV_ERR_WORKSPACE"]
+    assert sp(d, info(), ws=None) == ERR["PKV_ERR_WORKSPACE"]
+    assert sp(d, info(), ws=W + 8) == ERR["PKV_ERR_ALIGN"]
+    assert sp(d, info(), ws=PLAN - 64) == ERR["PKV_ERR_ALIAS"]
+    assert sp(d, info(), ws=E) == ERR["PKV_ERR_ALIAS"]
+    assert sp(d, info(), plan=A + 64) == ERR["PKV_ERR_ALIAS"]   # out overlaps the plan
+    # a plan with no set is the ordinary decode (here: its NULL check)
+    assert sp(d, info(G=0, M=0, maxm=0, tok=0), out=None) == ERR["PKV_ERR_NULL"]
+    assert sp(dims(S_=0), info(S_=0, G=0, M=0, maxm=0, tok=0), out=None) == 0

@@ -189,23 +189,36 @@ class Workload:
             self.num_kv_heads * self.head_dim * e * 2
 
 
-def _assign_blocks(rng, lens, bs, num_blocks, prefix_blocks=0):
-    """Physical placement: every sequence gets ceil(L/bs) blocks; the first
-    `prefix_blocks` logical blocks of every sequence are one shared set."""
+def _assign_blocks(rng, lens, bs, num_blocks, groups):
+    """Physical placement: every sequence gets ceil(L/bs) blocks.  `groups`
+    lists (members, prefix_blocks): the first prefix_blocks logical blocks
+    of every member of a group are one shared set of physical blocks; the
+    groups' sets come first in the draw, then every sequence's own blocks
+    in sequence order."""
     S = len(lens)
     need = [-(-int(L) // bs) for L in lens]
-    private = sum(max(0, n - prefix_blocks) for n in need)
-    total = prefix_blocks + private
+    pref = [0] * S
+    grp = [-1] * S
+    for gi, (members, pb) in enumerate(groups):
+        for s in members:
+            assert grp[s] < 0, "a sequence in two groups"
+            grp[s], pref[s] = gi, pb
+    shared_total = sum(pb for _, pb in groups)
+    private = sum(max(0, n - pref[s]) for s, n in enumerate(need))
+    total = shared_total + private
     if num_blocks is None:
         num_blocks = total
     assert num_blocks >= total
     ids = rng.permutation(num_blocks)[:total].astype(np.int32)
-    shared = ids[:prefix_blocks]
-    nxt = prefix_blocks
+    shared, nxt = [], 0
+    for _, pb in groups:
+        shared.append(ids[nxt:nxt + pb])
+        nxt += pb
     tables = []
     for s in range(S):
-        own = need[s] - prefix_blocks
-        tables.append(np.concatenate([shared, ids[nxt:nxt + own]]))
+        own = need[s] - pref[s]
+        pre = shared[grp[s]] if grp[s] >= 0 else ids[:0]
+        tables.append(np.concatenate([pre, ids[nxt:nxt + own]]))
         nxt += own
     return tables, num_blocks
 
@@ -215,24 +228,34 @@ def build(name: str, *, lens, num_heads: int, num_kv_heads: int,
           num_blocks=None, pool_factor: float = 1.0, max_blocks_per_seq=None,
           prefix_len: int = 0, key_outlier_frac: float = 0.0,
           key_outlier_mult: float = 8.0, scale=None, rng=None,
-          meta=None, chunk_lens=None) -> Workload:
+          meta=None, chunk_lens=None, prefix_groups=None) -> Workload:
     """Generic builder.  `lens` are the context lengths (new token
     included).  With prefix_len > 0 every sequence starts with the same
     prefix_len tokens held in shared blocks (prefix_len must be a multiple
-    of block_size).  The generator `rng` must already have drawn `lens` if
-    the caller drew them from it (placement continues the same stream).
-    With `chunk_lens` (C_s <= L_s per sequence) the workload is a chunked
-    prefill: q gets one row per chunk token."""
+    of block_size).  `prefix_groups` generalises this to several groups: a
+    list of (member sequences, prefix tokens), each group's prefix held once
+    in blocks its members share (members need at least that many tokens).
+    The generator `rng` must already have drawn `lens` if the caller drew
+    them from it (placement continues the same stream).  With `chunk_lens`
+    (C_s <= L_s per sequence) the workload is a chunked prefill: q gets one
+    row per chunk token."""
     rng = rng if rng is not None else np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     S = len(lens)
     bs = block_size
-    assert prefix_len % bs == 0 and (prefix_len == 0 or lens.min() > prefix_len)
-    pb = prefix_len // bs
+    if prefix_groups is None:
+        assert prefix_len % bs == 0 and (prefix_len == 0 or lens.min() > prefix_len)
+        prefix_groups = [(list(range(S)), prefix_len)] if prefix_len else []
+    else:
+        assert prefix_len == 0, "prefix_len or prefix_groups, not both"
+    groups = []
+    for members, plen in prefix_groups:
+        assert plen % bs == 0 and all(lens[m] >= plen for m in members)
+        groups.append((list(members), plen // bs))
     need_total = sum(-(-int(L) // bs) for L in lens)
     if num_blocks is None and pool_factor != 1.0:
         num_blocks = int(math.ceil(pool_factor * need_total))
-    tables, NB = _assign_blocks(rng, lens, bs, num_blocks, pb)
+    tables, NB = _assign_blocks(rng, lens, bs, num_blocks, groups)
     MB = max_blocks_per_seq or max(1, max(len(t) for t in tables))
     bt = np.full((S, MB), -1, np.int32)
     for s, t in enumerate(tables):
@@ -242,14 +265,20 @@ def build(name: str, *, lens, num_heads: int, num_kv_heads: int,
     for t in tables:
         np.add.at(refcount, t, 1)
 
-    # rows: the shared prefix once, then every sequence's own tokens
+    # rows: each group's shared prefix once, then every sequence's own tokens
+    base, R = [], 0
+    for _, pb in groups:
+        base.append(R)
+        R += pb * bs
+    pre_rows = [np.zeros(0, np.int64)] * S
+    for gi, (members, pb) in enumerate(groups):
+        for m in members:
+            pre_rows[m] = np.arange(base[gi], base[gi] + pb * bs, dtype=np.int64)
     rows_per_seq = []
-    R = prefix_len
-    for L in lens:
-        own = int(L) - prefix_len
+    for s, L in enumerate(lens):
+        own = int(L) - len(pre_rows[s])
         rows_per_seq.append(np.concatenate([
-            np.arange(prefix_len, dtype=np.int64),
-            np.arange(R, R + own, dtype=np.int64)]))
+            pre_rows[s], np.arange(R, R + own, dtype=np.int64)]))
         R += own
     Hq, Hkv, D = num_heads, num_kv_heads, head_dim
     qsl = None
