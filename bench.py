@@ -77,6 +77,13 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device copy "
                         "of this many MiB (to scale HBM counters)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="time the headline workload only (the default run "
+                        "also times the other decode workloads)")
+    p.add_argument("--reduce-counters", metavar="DIR", default=None,
+                   help="no GPU: turn the rocprofv3 runs under DIR (written by "
+                        "bench_probe/collect_counters.sh) into profiles/*.md "
+                        "and profiles/traffic.json")
     return p.parse_args()
 
 
@@ -118,11 +125,14 @@ def source_digest(kernel: str | None = None) -> str:
     if kernel is None:
         files = sorted(text)
     else:
-        pat = re.compile(rb"__global__[^;{]*?\b" + re.escape(kernel.encode())
-                         + rb"\s*\(", re.S)
-        files = [f for f in sorted(text) if pat.search(text[f])]
-        if not files:
-            raise ValueError(f"no kernel named {kernel} in {csrc}")
+        files = []
+        for k in kernel.split("+"):   # several kernels: "a+b"
+            pat = re.compile(rb"__global__[^;{]*?\b" + re.escape(k.encode())
+                             + rb"\s*\(", re.S)
+            found = [f for f in sorted(text) if pat.search(text[f])]
+            if not found:
+                raise ValueError(f"no kernel named {k} in {csrc}")
+            files += [f for f in found if f not in files]
         todo = list(files) + ["abi.hip"]
         files = []
         while todo:
@@ -161,6 +171,11 @@ def unique_kv_bytes(w, elem_bytes: int) -> int:
     return sum(live.values()) * w.num_kv_heads * w.head_dim * elem_bytes * 2
 
 
+def kernel_names(desc: str) -> list:
+    """The kernels of a roofline `kernel` description ("a (note) + b")."""
+    return [part.split()[0] for part in desc.split(" + ")]
+
+
 def stored_traffic(kernel: str, workload: str):
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
@@ -174,41 +189,42 @@ def stored_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path; "
-              "run it with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
+# The other decode workloads timed in the default run, after the headline
+# (13B-class multi-head) line: (workload, variant).
+EXTRA_CONFIGS = [("gqa70b", "single"), ("long_split", "split"),
+                 ("shared_prefix_bs16", "single"), ("shared_prefix_bs16", "shared"),
+                 ("shared_prefix_bs32", "single"), ("shared_prefix_bs32", "shared"),
+                 ("tiny", "single")]
 
+
+def decode_kernel_name(w, variant):
+    """The kernel the library picks: matrix cores for 2..16 query heads per
+    KV head in fp16/bf16, the vector kernel otherwise."""
+    k = ("decode_vector_kernel" if w.num_heads == w.num_kv_heads
+         or w.dtype == "f32" or w.num_heads // w.num_kv_heads > 16
+         else "decode_mfma_kernel")
+    if variant == "shared":
+        pre = ("decode_mfma_kernel (prefix partials)" if w.num_heads == w.num_kv_heads
+               else "prefill_mfma_kernel (prefix partials)")
+        return f"{pre} + {k}"
+    return k + (" + partition_reduce_kernel" if variant == "split" else "")
+
+
+def measure_decode(w, variant, partition, fp8, steps, warmup):
+    """One decode step (the cache write of every sequence's new token, then
+    attention) of workload w, timed: `steps` steps with no events in them,
+    then the same number with HIP events around each of the two launches on
+    the launch stream.  Returns the timings and the byte counts."""
     import numpy as np
     import torch
 
     import paged_kv_cache_309_amd as pkv
     import workloads as wl
 
-    torch.cuda.set_device(0)
-    if args.mode == "copy_blocks":
-        return bench_copy_blocks(args)
-    if args.mode == "swap":
-        return bench_swap(args)
-    if args.mode == "prefill":
-        return bench_prefill(args)
-    args.workload = args.workload or "mha13b"
-    if args.workload not in wl.CONFIGS:
-        raise SystemExit(f"{args.workload} is a prefill workload: use --mode prefill")
-    t0 = time.time()
-    w = wl.CONFIGS[args.workload](args.seed)
-    log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_heads} "
-        f"Hkv={w.num_kv_heads} D={w.head_dim} bs={w.block_size} "
-        f"dtype={w.dtype} NB={w.num_blocks} generated in {time.time()-t0:.1f}s")
-
     tdt = {"f32": torch.float32, "f16": torch.float16,
            "bf16": torch.bfloat16}[w.dtype]
-    fp8 = args.kv_dtype == "fp8"
     cdt = torch.float8_e4m3fn if fp8 else tdt
-    if args.variant == "shared" and (fp8 or w.dtype == "f32"):
+    if variant == "shared" and (fp8 or w.dtype == "f32"):
         raise SystemExit("--variant shared takes 16-bit caches and queries")
 
     def dev(a):
@@ -217,6 +233,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
+    t0 = time.time()
     q = dev(w.q)
     tables = torch.from_numpy(w.block_tables).cuda()
     lens = torch.from_numpy(w.context_lens).cuda()
@@ -233,10 +250,10 @@ def main():
     ws = None
     plan = None
     plan_ms = None
-    if args.variant == "split":
-        nbytes = pkv.split_workspace_bytes(q, k_cache, tables, args.partition)
+    if variant == "split":
+        nbytes = pkv.split_workspace_bytes(q, k_cache, tables, partition)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    elif args.variant == "shared":
+    elif variant == "shared":
         # the sharer sets, found on the host from the host tables (built by
         # the harness like the tables themselves; timed apart)
         t_plan = time.perf_counter()
@@ -248,7 +265,8 @@ def main():
             f"{plan.info.num_members} members, prefix "
             f"{plan.info.max_prefix_tokens} tokens, built in {plan_ms:.3f} ms")
     torch.cuda.synchronize()
-    log(f"[bench] inputs resident in HBM after {time.time()-t0:.1f}s")
+    log(f"[bench] {w.name} ({variant}) inputs resident in HBM after "
+        f"{time.time()-t0:.1f}s")
 
     stream = torch.cuda.current_stream()
     ev = []
@@ -260,21 +278,21 @@ def main():
         pkv.reshape_and_cache(new_k, new_v, k_cache, v_cache, new_slots)
         if record:
             e[1].record(stream)
-        if args.variant == "single":
+        if variant == "single":
             pkv.paged_attention_decode(out, q, k_cache, v_cache, tables, lens,
                                        w.scale)
-        elif args.variant == "shared":
+        elif variant == "shared":
             pkv.paged_attention_decode_shared_prefix(out, q, k_cache, v_cache,
                                                      tables, lens, w.scale,
                                                      plan, ws)
         else:
             pkv.paged_attention_decode_split(out, q, k_cache, v_cache, tables,
-                                             lens, w.scale, args.partition, ws)
+                                             lens, w.scale, partition, ws)
         if record:
             e[2].record(stream)
             ev.append(e)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
@@ -282,50 +300,108 @@ def main():
     # the timed steps carry the work only; the launch times of the two
     # kernels come from a second pass with events between the launches
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(False)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
     rac_ms = [e[0].elapsed_time(e[1]) for e in ev]
     att_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    log(f"[bench] {args.steps} steps in {total_ms:.2f} ms")
-
-    calibration_copy(args.calib_copy_mib)
-    ceiling = read_ceiling()
+    log(f"[bench] {w.name} ({variant}): {steps} steps in {total_ms:.2f} ms")
+    del k_cache, v_cache, ws, out, q
+    torch.cuda.empty_cache()
 
     e = np.dtype(wl.STORAGE[w.dtype]).itemsize
     kv_bytes = w.kv_bytes(1 if fp8 else None)
     # the roofline counts each physical K/V byte once: shared prefix blocks
-    # are read by every sharer but held once (served from cache after the
-    # first read); the metric's effective GB/s stays on logical bytes
+    # are read by every sharer but held once; the metric's effective GB/s
+    # stays on logical bytes
     kv_unique = unique_kv_bytes(w, 1 if fp8 else e)
     nblk = int(sum(-(-int(L) // w.block_size) for L in w.context_lens))
     qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
     table_bytes = 4 * nblk + 4 * w.num_seqs
-    att_alg_bytes = kv_unique + qo_bytes + table_bytes
+    return {"ms_step": total_ms / steps, "att_ms": att_ms, "rac_ms": rac_ms,
+            "kv_bytes": kv_bytes, "kv_unique": kv_unique,
+            "alg_bytes": kv_unique + qo_bytes + table_bytes, "plan_ms": plan_ms}
+
+
+def config_summary(w, variant, partition, fp8, m):
+    """The per-workload figures of the default run's `configs` object."""
+    import numpy as np
+    att = float(np.mean(m["att_ms"]))
+    kernel = decode_kernel_name(w, variant)
+    tag = w.name + ("_fp8" if fp8 else "")
+    traffic = stored_traffic("+".join(kernel_names(kernel)), tag)
+    return {
+        "variant": variant, "partition": partition if variant == "split" else None,
+        "kernel": kernel,
+        "attention_us": round(att * 1e3, 2),
+        "attention_median_us": round(float(np.median(m["att_ms"])) * 1e3, 2),
+        "step_us": round(m["ms_step"] * 1e3, 2),
+        "kv_gbs": round(m["kv_bytes"] / (att * 1e-3) / 1e9, 1),
+        "roofline_frac": round(m["alg_bytes"] / (att * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic_ratio": (round(traffic / m["alg_bytes"], 4) if traffic else None),
+        "kv_bytes": m["kv_bytes"], "kv_bytes_unique": m["kv_unique"],
+        "decode_tokens_per_s": round(w.num_seqs / (m["ms_step"] * 1e-3), 1),
+        "prefix_plan_ms": round(m["plan_ms"], 4) if m["plan_ms"] is not None else None,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path; "
+              "run it with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.reduce_counters:
+        return reduce_counters(args.reduce_counters)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_309_amd as pkv  # noqa: F401  (fails if not built)
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    if args.mode == "copy_blocks":
+        return bench_copy_blocks(args)
+    if args.mode == "swap":
+        return bench_swap(args)
+    if args.mode == "prefill":
+        return bench_prefill(args)
+    headline = args.workload is None
+    args.workload = args.workload or "mha13b"
+    if args.workload not in wl.CONFIGS:
+        raise SystemExit(f"{args.workload} is a prefill workload: use --mode prefill")
+    t0 = time.time()
+    w = wl.CONFIGS[args.workload](args.seed)
+    log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_heads} "
+        f"Hkv={w.num_kv_heads} D={w.head_dim} bs={w.block_size} "
+        f"dtype={w.dtype} NB={w.num_blocks} generated in {time.time()-t0:.1f}s")
+    fp8 = args.kv_dtype == "fp8"
+    m = measure_decode(w, args.variant, args.partition, fp8, args.steps, args.warmup)
+
+    calibration_copy(args.calib_copy_mib)
+    ceiling = read_ceiling()
+
+    kv_bytes, kv_unique, att_alg_bytes = m["kv_bytes"], m["kv_unique"], m["alg_bytes"]
+    ms_step = m["ms_step"]
+    att_ms, rac_ms = m["att_ms"], m["rac_ms"]
     att_mean_ms = float(np.mean(att_ms))
     achieved = att_alg_bytes / (att_mean_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     tok_s = w.num_seqs / (ms_step * 1e-3)
-    # the kernel the library picks: matrix cores for 2..16 query heads per
-    # KV head in fp16/bf16, the vector kernel otherwise
-    kernel = ("decode_vector_kernel" if w.num_heads == w.num_kv_heads
-              or w.dtype == "f32" or w.num_heads // w.num_kv_heads > 16
-              else "decode_mfma_kernel")
+    kernel = decode_kernel_name(w, args.variant)
     tag = w.name + ("_fp8" if fp8 else "")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(kernel, tag),
-                "kernel": ("prefill_mfma_kernel (prefix partials) + " if
-                           args.variant == "shared" else "") + kernel +
-                          {"single": "", "shared": "",
-                           "split": " + partition_reduce_kernel"}[args.variant],
+                "traffic": stored_traffic("+".join(kernel_names(kernel)), tag),
+                "kernel": kernel,
                 "algorithmic_bytes_per_launch": att_alg_bytes,
                 "mean_launch_ms": round(att_mean_ms, 5),
                 "logical_kv_gbs": round(kv_bytes / (att_mean_ms * 1e-3) / 1e9, 1)}
@@ -334,6 +410,23 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, kv_bytes, fp8)
         cpu["gpu_speedup"] = round(value / cpu["value"], 1)
+
+    configs = None
+    if headline and not args.no_configs and not fp8 and args.variant == "single":
+        # the other workloads, each timed the same way after the headline,
+        # with at least 50 warm-up and 50 timed steps: the workloads served
+        # from L2 and the MALL (shared prefixes) read up to 13% slow in the
+        # first tens of steps
+        configs = {"steps": max(args.steps, 50), "warmup": max(args.warmup, 50)}
+        for name, variant in EXTRA_CONFIGS:
+            t1 = time.time()
+            wx = wl.CONFIGS[name](args.seed)
+            log(f"[bench] config {name} ({variant}) generated in {time.time()-t1:.1f}s")
+            mx = measure_decode(wx, variant, args.partition, False, configs["steps"],
+                                configs["warmup"])
+            configs[f"{name}:{variant}"] = config_summary(wx, variant, args.partition,
+                                                          False, mx)
+            del wx
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
@@ -350,7 +443,8 @@ def main():
                    "variant": args.variant,
                    "kv_dtype": "e4m3" if fp8 else w.dtype,
                    "partition": args.partition if args.variant == "split" else None,
-                   "prefix_plan_ms": round(plan_ms, 4) if plan_ms is not None else None,
+                   "prefix_plan_ms": (round(m["plan_ms"], 4)
+                                      if m["plan_ms"] is not None else None),
                    "accumulate": "f32", "kv_bytes_per_step": kv_bytes,
                    "kv_bytes_unique_per_step": kv_unique},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -367,8 +461,136 @@ def main():
                             "arithmetic) on this GPU, for comparison with "
                             "roofline.achieved; null if its helper is not built"},
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(rec), flush=True)
+
+
+def _find(d, suffix):
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    return f[0] if f else None
+
+
+def _last_json(path):
+    for line in reversed(open(path).read().splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    return None
+
+
+def _counter(d, name):
+    """Per-kernel lists of one counter's per-dispatch values (rocprofv3 CSV)."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] == name:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(vals, sub):
+    return [x for k, v in vals.items() if sub in k for x in v]
+
+
+def reduce_counters(root):
+    """Turn rocprofv3 runs into profiles/<kernel>_<workload>.md summaries and
+    profiles/traffic.json.  `root` holds one folder per workload, as
+    bench_probe/collect_counters.sh writes them: args.txt (the bench
+    arguments), kt.json + kt/ (a --kernel-trace --stats run), and FETCH_SIZE/,
+    WRITE_SIZE/ (one --pmc pass each, every run ending with a plain 1 GiB
+    device copy).  HBM bytes per launch = the kernel's mean counter value in
+    KiB x 1024 x (1 GiB / the copy's reading of the same counter)."""
+    import csv
+    tj = os.path.join(PROFILES, "traffic.json")
+    traffic = json.load(open(tj)) if os.path.exists(tj) else {}
+    for tag in sorted(os.listdir(root)):
+        d = os.path.join(root, tag)
+        if not os.path.exists(os.path.join(d, "args.txt")):
+            continue
+        args = open(os.path.join(d, "args.txt")).read().strip()
+        rec = _last_json(os.path.join(d, "kt.json"))
+        roof = rec["roofline"]
+        kernels = kernel_names(roof["kernel"])
+        kernel = "+".join(kernels)
+        wtag = rec["config"]["workload"] + ("_fp8" if "e4m3" in rec["dtype"] else "")
+        if kernel == "copy_blocks_kernel":
+            wtag = rec["config"]["workload"]
+        stats = list(csv.DictReader(open(_find(os.path.join(d, "kt"), "kernel_stats.csv"))))
+        kt_cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
+                  "--output-format csv -d <out> -o run -- python3 <repo>/bench.py "
+                  f"--steps 50 --warmup 5 --no-cpu-baseline {args}").strip()
+
+        def pmc_cmd(c):
+            return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc "
+                    f"{c} --output-format csv -d <out> -o run -- python3 "
+                    "<repo>/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+                    f"--calib-copy-mib 1024 {args}").strip()
+        L = [f"# {kernel} on the {wtag} workload", "",
+             "Kernel-trace statistics (run from the repository root on one MI355X; "
+             "`bench_probe/collect_counters.sh` runs these commands, "
+             "`python bench.py --reduce-counters <out>` writes this file):",
+             "", "```", kt_cmd, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+        for r in stats:
+            name = r["Name"]
+            short = (name[5:] if name.startswith("void ") else name).split("(")[0]
+            if "read_tiles_kernel" in name:
+                short = ("read_tiles_kernel (bench_probe: random 4 KiB tile read "
+                         "ceiling, context only)")
+            L.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+        L.append("")
+        if any("reshape_and_cache" in r["Name"] for r in stats):
+            L += ["The reshape_and_cache average includes the one large call that "
+                  "fills the earlier context; the per-step calls are the minimum.", ""]
+        mean_us = roof["mean_launch_ms"] * 1e3
+        unit = roof["unit"]
+        L.append(f"bench.py in the same run (HIP events on the launch stream): mean "
+                 f"launch {mean_us:.1f} us, roofline {roof['achieved']:.0f} {unit} = "
+                 f"{100*roof['frac']:.1f}% of {roof['peak']:.0f} {unit}, step "
+                 f"{rec['ms_per_step']*1e3:.1f} us.")
+        L += ["", "HBM traffic per launch, from two counter passes:", "", "```",
+              pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE"), "```", ""]
+        f = _counter(os.path.join(d, "FETCH_SIZE"), "FETCH_SIZE")
+        wr = _counter(os.path.join(d, "WRITE_SIZE"), "WRITE_SIZE")
+        cf, cw = max(_pick(f, "copyBuffer")), max(_pick(wr, "copyBuffer"))
+        kf, kw = 1048576.0 / cf, 1048576.0 / cw
+        L.append(f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {cf:.0f} KiB "
+                 f"and WRITE_SIZE = {cw:.0f} KiB, so the counters are scaled by "
+                 f"{kf:.3f} and {kw:.3f}.")
+        # every launch of the attention: the mean per dispatch of each kernel,
+        # added up
+        fr = sum(sum(_pick(f, k)) / len(_pick(f, k)) for k in kernels)
+        wrr = sum(sum(_pick(wr, k)) / len(_pick(wr, k)) for k in kernels)
+        rb, wb = fr * 1024 * kf, wrr * 1024 * kw
+        L += ["", "| kernel | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | read bytes "
+              "(scaled) | written bytes (scaled) | algorithmic bytes | traffic / "
+              "algorithmic |", "|---|---|---|---|---|---|---|"]
+        if "algorithmic_bytes_per_launch" in roof:
+            alg = roof["algorithmic_bytes_per_launch"]
+            L.append(f"| `{kernel}` | {fr:.0f} | {wrr:.1f} | {rb:.4g} | {wb:.4g} | "
+                     f"{alg:.4g} | {(rb+wb)/alg:.3f} |")
+        else:
+            L.append(f"| `{kernel}` | {fr:.0f} | {wrr:.1f} | {rb:.4g} | {wb:.4g} | "
+                     f"(flop-bound: {roof['algorithmic_flops_per_launch']:.4g} flops) | - |")
+        L.append("")
+        open(os.path.join(PROFILES, f"{kernel}_{wtag}.md"), "w").write("\n".join(L))
+        traffic[f"{kernel}:{wtag}"] = {
+            "bytes_per_launch": int(round(rb + wb)), "read_bytes": int(round(rb)),
+            "write_bytes": int(round(wb)), "fetch_size_kib_raw": fr,
+            "write_size_kib_raw": wrr, "calibration_factor_fetch": kf,
+            "calibration_factor_write": kw, "source_digest": source_digest(kernel),
+            "commands": [c.replace("cd /tmp && export TMPDIR=/tmp && ", "")
+                         .replace("--output-format csv -d <out> -o run ", "... ")
+                         .replace("<repo>/", "")
+                         for c in (pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE"))]}
+        print(f"{tag}: {kernel} on {wtag}, mean launch {mean_us:.1f} us, traffic / "
+              f"algorithmic {(rb + wb) / roof.get('algorithmic_bytes_per_launch', float('nan')):.3f}",
+              flush=True)
+    json.dump(traffic, open(tj, "w"), indent=1)
 
 
 def read_ceiling():

@@ -81,3 +81,52 @@ def test_unique_kv_bytes_count_a_shared_prefix_once():
     tokens = 64 + sum(L - 64 for L in lens)
     assert bench.unique_kv_bytes(w, 2) == tokens * 2 * 64 * 2 * 2
     assert bench.unique_kv_bytes(w, 2) < w.kv_bytes()
+
+
+def test_reduce_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    """A synthetic pair of counter passes: the kernel's mean reading in KiB,
+    times 1024, times 1 GiB over the copy's reading, per launch; kernels of
+    one attention (here the split's partial and reduce kernels) add up."""
+    root = tmp_path / "runs"
+    d = root / "ls"
+    (d / "kt").mkdir(parents=True)
+    (d / "FETCH_SIZE").mkdir()
+    (d / "WRITE_SIZE").mkdir()
+    (d / "args.txt").write_text("--workload long_split --variant split")
+    rec = {"metric": "m", "ms_per_step": 0.7, "dtype": "bf16",
+           "config": {"workload": "long_split"},
+           "roofline": {"kernel": "decode_vector_kernel + partition_reduce_kernel",
+                        "mean_launch_ms": 0.68, "achieved": 6300.0, "frac": 0.79,
+                        "peak": 8000.0, "unit": "GB/s",
+                        "algorithmic_bytes_per_launch": 4.0e9}}
+    (d / "kt.json").write_text("noise\n" + json.dumps(rec) + "\n")
+    (d / "kt" / "run_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void pkv::decode_vector_kernel<2, 2, 128, 16, true, false>(pkv::DecodeArgs)",'
+        '50,33000000,660000,97.0,650000,700000,1000\n')
+
+    def passes(counter, kern_vals, copy_val):
+        rows = ["Kernel_Name,Counter_Name,Counter_Value"]
+        for name, vals in kern_vals.items():
+            rows += [f'"{name}",{counter},{v}' for v in vals]
+        rows.append(f'"__amd_rocclr_copyBuffer",{counter},{copy_val}')
+        return "\n".join(rows) + "\n"
+    vk = "void pkv::decode_vector_kernel<2, 2, 128, 16, true, false>(pkv::DecodeArgs)"
+    rk = "void pkv::partition_reduce_kernel<2, 128>(pkv::DecodeArgs)"
+    (d / "FETCH_SIZE" / "run_counter_collection.csv").write_text(
+        passes("FETCH_SIZE", {vk: [2000000, 2000002], rk: [4000]}, 524288))
+    (d / "WRITE_SIZE" / "run_counter_collection.csv").write_text(
+        passes("WRITE_SIZE", {vk: [8000], rk: [64]}, 1048576))
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "PROFILES", str(prof))
+    bench.reduce_counters(str(root))
+    t = json.load(open(prof / "traffic.json"))
+    e = t["decode_vector_kernel+partition_reduce_kernel:long_split"]
+    assert e["calibration_factor_fetch"] == 2.0 and e["calibration_factor_write"] == 1.0
+    assert e["read_bytes"] == round((2000001 + 4000) * 1024 * 2.0)
+    assert e["write_bytes"] == (8000 + 64) * 1024
+    assert e["source_digest"] == bench.source_digest(
+        "decode_vector_kernel+partition_reduce_kernel")
+    md = (prof / "decode_vector_kernel+partition_reduce_kernel_long_split.md").read_text()
+    assert "--workload long_split --variant split" in md and "| 50 | 660.0 |" in md
