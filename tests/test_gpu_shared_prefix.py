@@ -217,3 +217,19 @@ def test_refusals():
             torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
     assert e.value.status == 2   # fp32 queries: use the ordinary decode
     torch.cuda.synchronize()
+
+
+INST = [(dt, D, bs, G) for dt in ("f16", "bf16") for D in (64, 128)
+        for bs in (16, 32) for G in (1, 4)]
+
+
+@pytest.mark.parametrize("dt,D,bs,G", INST, ids=[f"{a}-D{b}-bs{c}-G{d}" for a, b, c, d in INST])
+def test_every_instantiation(dt, D, bs, G):
+    """Each compiled prefix kernel (multi-head: member columns; grouped-query:
+    chunked rows) and its decode kernel, once, on a small ragged case with
+    two sets and a sequence that shares nothing."""
+    seed = 900 + INST.index((dt, D, bs, G))
+    w = groups_case(seed, S=9, Hq=2 * G, Hkv=2, D=D, bs=bs, dtype=dt, n_groups=2,
+                    max_prefix_blocks=6, max_suffix=70, unshared=1)
+    plan, _ = check_case(w, f"instantiation {dt} D{D} bs{bs} G{G}")
+    assert plan.info.num_groups == 2
