@@ -34,10 +34,13 @@
 // the probabilities stay in the lanes that computed them.  Its A operand
 // (V^T: dim rows, token columns) then needs, per lane, four consecutive
 // tokens of one dim from each tile, which the token-grouped V layout stores
-// as 8 contiguous bytes; dims 32u + 2m + j (j = 0, 1) make it one 16-byte
-// LDS read per tile for two n-tiles.  K rows are stored with their 16-byte
-// chunks permuted (see PrefillRing) so that lanes reading different token
-// rows use different banks.
+// as 8 contiguous bytes.  N-tile 2u + j takes dims 32u + 16j + m (m = 0 ..
+// 15), so the 16 lanes of one token group read 16 consecutive 8-byte words
+// (every LDS bank once; dims 32u + 2m + j, two n-tiles per 16 bytes, left
+// every other bank idle and doubled the value reads' time), and each lane's
+// four output rows are four adjacent dims.  K rows are stored with their
+// 16-byte chunks permuted (see PrefillRing) so that lanes reading different
+// token rows use different banks.
 //
 // Scheduling: workgroup i runs on XCD i % 8.  All row blocks of one
 // (sequence, KV head) are given consecutive workgroup numbers on one XCD,
@@ -101,6 +104,14 @@ struct PrefillRing {
   static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;
   static constexpr int LOADS = PIECE / 1024;  // per wavefront and super-tile
   __device__ static __forceinline__ int key(int r) { return (r / RPL) % CR; }
+  // V pieces of 16-bit caches: the 16-byte chunks (two dims of one token
+  // group) of odd token groups trade places with the chunk 128 bytes away,
+  // so the two token groups of one 32-lane pass of 8-byte reads (lanes
+  // reading 16 consecutive dims each) fill all 64 banks.  Byte offset of
+  // dim d of token group g inside the piece.
+  __device__ static __forceinline__ int voff(int g, int d) {
+    return g * D * 8 + (((d >> 1) ^ ((g & 1) << 3)) << 4) + (d & 1) * 8;
+  }
 };
 
 __device__ __forceinline__ u32x4 lds16(const char *p) {
@@ -276,8 +287,15 @@ prefill_mfma_kernel(PrefillArgs a) {
       const int rows_per_kib = 1024 / RG::ROWB;
       const int r = b * rows_per_kib + lane / RG::CR, p = lane % RG::CR;
       lane_off[b] = (uint32_t)(r * RG::ROWB + ((p ^ RG::key(r)) * 16));
-    } else {
+    } else if constexpr (F8) {
       lane_off[b] = (uint32_t)(b * 1024 + lane * 16);
+    } else {
+      // LDS chunk c = 64b + lane is chunk cg = c % (D/2) of token group
+      // g = c / (D/2); by voff it holds that group's dims 2(cg ^ x) and
+      // 2(cg ^ x) + 1, x = 8 (g odd) or 0, which sit 16 (cg ^ x) bytes into
+      // the group in the cache's layout
+      const int c = b * 64 + lane, g = c / (D / 2), cg = c % (D / 2);
+      lane_off[b] = (uint32_t)(g * D * 8 + ((cg ^ ((g & 1) << 3)) << 4));
     }
   }
   // physical block of this wavefront's piece of super-tile n (a tile past
@@ -377,14 +395,16 @@ prefill_mfma_kernel(PrefillArgs a) {
           kop[st][kk] = lds16(base + st * RG::PIECE + col * RG::ROWB + ((c ^ RG::key(col)) * 16));
         }
       if (MAY_TAIL && 32 * n + 32 > L) zero_tail_keys(kop, n);
-      // value operand of n-tile 2u+j: dim 32u + 2*col + j, four tokens of
+      // value operand of n-tile 2u+j: dim 32u + 16j + col, four tokens of
       // tile 0 then the same four of tile 1 (8 bytes each, one piece apart,
-      // so one two-address LDS read fills the operand's registers in place)
+      // so one two-address LDS read fills the operand's registers in place;
+      // the 16 lanes of a token group read 128 consecutive bytes, and the
+      // two groups of a 32-lane pass different halves of the banks)
 #pragma unroll
       for (int u = 0; u < NC; ++u)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const char *v0 = base + 2 * RG::PIECE + (grp * D + 32 * u + 2 * col) * 8 + 8 * j;
+          const char *v0 = base + 2 * RG::PIECE + RG::voff(grp, 32 * u + 16 * j + col);
           const u32x2 lo = *(const volatile __attribute__((address_space(3))) u32x2 *)v0;
           const u32x2 hi = *(const volatile __attribute__((address_space(3))) u32x2 *)(v0 + RG::PIECE);
           va[2 * u + j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -561,9 +581,9 @@ prefill_mfma_kernel(PrefillArgs a) {
     // the partial state of each row: maximum (log2 units), sum of the
     // weights and weighted sum of values, un-normalised; every row of a
     // chunk saw at least one token, so its maximum is finite.  Row m =
-    // 4*grp + i of n-tile 2u+j is dim 32u + 2m + j (16-bit caches; two
-    // adjacent dims stored together), of n-tile 4u+j dim 64u + 4m + j
-    // (8-bit caches; four adjacent dims stored together).
+    // 4*grp + i of n-tile 2u+j is dim 32u + 16j + m (16-bit caches; the
+    // lane's four rows are four adjacent dims), of n-tile 4u+j dim
+    // 64u + 4m + j (8-bit caches; four adjacent dims stored together).
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
       if (row0 + qt * 16 + col > row_last) continue;  // no row in this column
@@ -581,24 +601,19 @@ prefill_mfma_kernel(PrefillArgs a) {
                 f32x4{acc[qt][4 * u][i], acc[qt][4 * u + 1][i], acc[qt][4 * u + 2][i],
                       acc[qt][4 * u + 3][i]};
       } else {
-        // dims 32u + 8*grp .. +7 of the row are this lane's (i, j) = (0, 0),
-        // (0, 1), (1, 0), ...: two 16-byte stores
+        // n-tile t: dims 32(t/2) + 16(t%2) + 4*grp .. +3, one 16-byte store
 #pragma unroll
-        for (int u = 0; u < NC; ++u)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            *reinterpret_cast<f32x4 *>(po + 32 * u + 8 * grp + 4 * hf) =
-                f32x4{acc[qt][2 * u][2 * hf], acc[qt][2 * u + 1][2 * hf],
-                      acc[qt][2 * u][2 * hf + 1], acc[qt][2 * u + 1][2 * hf + 1]};
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<f32x4 *>(po + 32 * (t / 2) + 16 * (t % 2) + 4 * grp) = acc[qt][t];
       }
     }
     return;
   }
 
   // normalise and store: row m = 4*grp + i of n-tile 2u+j is dim
-  // 32u + 2m + j of the lane's query row (16-bit caches; two adjacent dims
-  // stored as one 32-bit word), of n-tile 4u+j dim 64u + 4m + j (8-bit
-  // caches; four adjacent dims stored as one 64-bit word)
+  // 32u + 16j + m of the lane's query row (16-bit caches), of n-tile 4u+j
+  // dim 64u + 4m + j (8-bit caches); either way the lane holds four
+  // adjacent dims, stored as one 64-bit word
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const float lt = lsum[qt][0];
@@ -619,13 +634,13 @@ prefill_mfma_kernel(PrefillArgs a) {
         }
     } else {
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * u + 2 * (4 * grp + i);
-          op[d >> 1] = from_f32<QT>(acc[qt][2 * u][i] * inv) |
-                       (from_f32<QT>(acc[qt][2 * u + 1][i] * inv) << 16);
-        }
+      for (int t = 0; t < NT; ++t) {
+        const int d = 32 * (t / 2) + 16 * (t % 2) + 4 * grp;
+        const u32x2 wv = {from_f32<QT>(acc[qt][t][0] * inv) |
+                              (from_f32<QT>(acc[qt][t][1] * inv) << 16),
+                          from_f32<QT>(acc[qt][t][2] * inv) |
+                              (from_f32<QT>(acc[qt][t][3] * inv) << 16)};
+        *reinterpret_cast<u32x2 *>(op + (d >> 1)) = wv;
       }
     }
   }
