@@ -155,6 +155,45 @@ def test_calls_in_a_row_on_one_workspace(Hkv):
         assert np.array_equal(pool_bits(out), alone[i % len(runs)]), i
 
 
+def test_calls_repeat_bit_for_bit_whatever_the_workspace_holds():
+    """The same multi-head call 24 times on one workspace, which between
+    calls holds random bytes, 0xff, zeros or what the last call left
+    (suffixes of 1 to 600 tokens after prefixes of up to 768): every output
+    bit for bit the first one, which matches the oracle."""
+    import paged_kv_cache_309_amd as pkv
+    w = groups_case(61, S=48, Hq=8, Hkv=8, D=128, bs=16, dtype="bf16", n_groups=3,
+                    max_prefix_blocks=48, max_suffix=600, unshared=3)
+    kc, vc = nan_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    plan = pkv.PrefixPlan(w.block_tables, w.context_lens, w.block_size)
+    need = pkv.shared_prefix_workspace_bytes(dev.q, kd, dev.block_tables, plan)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    print(f"[shared prefix] repeats: S={w.num_seqs} sets="
+          f"{plan.info.num_groups}", flush=True)
+    first = None
+    for rep in range(24):
+        kind = rep % 4
+        if kind == 0:
+            ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda",
+                                   generator=gen))
+        elif kind == 1:
+            ws.fill_(255)
+        elif kind == 2:
+            ws.zero_()
+        out = torch.full_like(dev.q, float("nan"))
+        pkv.paged_attention_decode_shared_prefix(out, dev.q, kd, vd, dev.block_tables,
+                                                 dev.context_lens, w.scale, plan, ws)
+        torch.cuda.synchronize()
+        bits = pool_bits(out)
+        if first is None:
+            first = bits
+            compare(to_f64(out), want, w.dtype, "shared-prefix decode, repeated")
+        assert np.array_equal(bits, first), rep
+
+
 def test_one_hot_probe_through_the_prefix_is_bit_exact():
     """q = e0, keys zero except a huge first component at one position:
     every weight but that token's underflows to exactly 0, so the output is
@@ -193,10 +232,12 @@ def test_one_hot_probe_through_the_prefix_is_bit_exact():
         assert np.array_equal(got, want), pos
 
 
-def test_physical_permutation_is_bitwise_invariant():
+@pytest.mark.parametrize("Hkv", [2, 8])
+def test_physical_permutation_is_bitwise_invariant(Hkv):
     """Moving every block to another physical place (tables rewritten)
-    leaves the output bit for bit the same."""
-    w = groups_case(21, S=16, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", n_groups=2,
+    leaves the output bit for bit the same (grouped-query: chunked prefix
+    products; multi-head: members as the products' columns)."""
+    w = groups_case(21, S=16, Hq=8, Hkv=Hkv, D=128, bs=16, dtype="bf16", n_groups=2,
                     max_prefix_blocks=20, max_suffix=200)
     kc, vc = nan_pool(w)
     dev = Dev(w)
