@@ -44,6 +44,19 @@ def test_stored_traffic_keys_name_real_kernels():
         assert workload
 
 
+def test_stored_traffic_was_read_from_the_current_kernels():
+    """Every stored HBM-counter reading (and the profile beside it) was taken
+    on kernels whose code is the code in the tree: a kernel changed since its
+    counters were read must be profiled again (bench_probe/collect_counters.sh,
+    then bench.py --reduce-counters)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        pytest.skip("no stored counter readings")
+    stale = [key for key, rec in json.load(open(path)).items()
+             if rec["source_digest"] != bench.source_digest(key.split(":")[0])]
+    assert not stale, f"counter readings older than their kernels: {stale}"
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True,
