@@ -10,6 +10,7 @@ Every result must equal the oracle's on the compact pool:
 - decode, single pass and split, on the vector and matrix-core kernels,
   over 16-bit, fp32 and 8-bit caches;
 - chunked prefill;
+- the shared-prefix decode (both prefix kernels);
 - the cache write (bit-exact);
 - the block copy (bit-exact);
 - the swap out to pinned host memory and back (bit-exact).
@@ -187,6 +188,44 @@ def test_prefill_past_4gib(dt, Hq, Hkv, cache):
     got = to_f64(out)
     assert np.all(np.isfinite(got))
     compare(got, want, dt, f"prefill past 4 GiB {dt} {cache}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2)])
+def test_shared_prefix_past_4gib(Hq, Hkv):
+    """The shared-prefix decode over blocks past the 4 GiB mark: the prefix
+    products (multi-head: members as the columns; grouped-query: the chunked
+    products) and the decode of the rest, against the oracle's decode on the
+    compact pool."""
+    import paged_kv_cache_309_amd as pkv
+    D, bs, dt = 128, 16, "bf16"
+    seed = 8500 + Hkv
+    rng = np.random.default_rng(seed)
+    lens = np.concatenate([rng.integers(1, 120, 6) + 320, rng.integers(1, 90, 4) + 160,
+                           rng.integers(1, 400, 2)])
+    w = wl.build(f"large_prefix{Hkv}", lens=lens, num_heads=Hq, num_kv_heads=Hkv,
+                 head_dim=D, block_size=bs, dtype=dt, seed=seed, pool_factor=1.5,
+                 prefix_groups=[([0, 1, 2, 3, 4, 5], 320), ([6, 7, 8, 9], 160)], rng=rng)
+    kc, vc = compact_pools(w, "same")
+    kd, vd, ids = big_pools(w, "same", kc, vc, seed)
+    bt_host = remap_table(w.block_tables, ids)
+    plan = pkv.PrefixPlan(bt_host, w.context_lens, bs)
+    assert plan.info.num_groups == 2
+    print(f"[large pool shared prefix] Hq={Hq} Hkv={Hkv} pool={kd.shape[0]} blocks "
+          f"ids {ids.min()}..{ids.max()}", flush=True)
+    q = to_torch(w.q, dt)
+    out = torch.full_like(q, float("nan"))
+    bt = torch.from_numpy(bt_host).cuda()
+    ws = torch.empty(max(pkv.shared_prefix_workspace_bytes(q, kd, bt, plan), 16),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_decode_shared_prefix(out, q, kd, vd, bt,
+                                             torch.from_numpy(w.context_lens).cuda(),
+                                             w.scale, plan, ws)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                               bs, Hkv, w.num_blocks, dt)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    compare(got, want, dt, f"shared-prefix decode past 4 GiB Hq={Hq} Hkv={Hkv}")
 
 
 @pytest.mark.parametrize("dt,cache", [("bf16", "same"), ("f16", "fp8")])
