@@ -278,6 +278,26 @@ def test_very_wide_block_table():
     compare(to_f64(dev.decode(kd, vd)), want, "bf16", "wide table")
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 8, 2), ("f16", 2, 2)])
+def test_quarter_million_token_contexts(dtype, Hq, Hkv):
+    """Contexts of 262144 and 200001 tokens (16384 and 12501 blocks of 16),
+    single pass and split at 512-token partitions, on the matrix-core (GQA)
+    and the vector (MHA) kernel: every output against the oracle.  Token,
+    tile and partition indices reach 2^18, byte offsets inside one
+    sequence's table 2^16."""
+    lens = [262144, 200001]
+    w = wl.build(f"long{Hq}", lens=lens, num_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                 block_size=16, dtype=dtype, seed=9300 + Hq, pool_factor=1.05)
+    print_case("quarter-million tokens", w)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    for variant in ("single", "split"):
+        got = to_f64(dev.decode(kd, vd, variant=variant, partition=512))
+        compare(got, want, dtype, f"quarter-million tokens {variant}")
+
+
 @pytest.mark.parametrize("S", [1, 255, 256, 257, 1024, 4097])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
 def test_longest_first_order_covers_every_sequence(S, Hq, Hkv):
