@@ -97,15 +97,15 @@ int paged_attention_shared_prefix_workspace_bytes(const pkv_dims *dims, int bloc
  * described here, but give unspecified results.
  *
  * Two launches: the prefix products on the matrix cores (for multi-head
- * attention, blocks of 16 members of a set as the columns of the products,
- * one partial per (member, head); for grouped-query attention, blocks of
- * 128 (member, query head) rows against chunks of the prefix staged in
- * LDS, one partial per chunk), then the decode kernel over each sequence's
- * tokens after its prefix, which starts from the prefix partials.  In the
- * prefix products the probabilities enter the value product rounded to the
- * query type and the sums add exactly those rounded weights; accumulation
- * is fp32.  fp32 queries are refused (PKV_ERR_DTYPE): use
- * paged_attention_decode.  workspace: device memory of at least
+ * attention, blocks of 32 members of a set as the columns of the products,
+ * one partial per (member, head, chunk of the prefix); for grouped-query
+ * attention, blocks of 128 (member, query head) rows against chunks of the
+ * prefix staged in LDS, one partial per chunk), then the decode kernel over
+ * each sequence's tokens after its prefix, which starts from the prefix
+ * partials.  In the prefix products the probabilities enter the value
+ * product rounded to the query type and the sums add exactly those rounded
+ * weights; accumulation is fp32.  fp32 queries are refused
+ * (PKV_ERR_DTYPE): use paged_attention_decode.  workspace: device memory of at least
  * paged_attention_shared_prefix_workspace_bytes (contents on entry do not
  * matter; it must not overlap any other argument).  A plan with no set
  * runs paged_attention_decode.  Everything else as paged_attention_decode.

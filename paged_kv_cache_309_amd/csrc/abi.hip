@@ -356,17 +356,18 @@ constexpr int kPrefixMaxChunks = 16;  // the vector decode kernel's row states
 constexpr int kPrefixMemberTarget = 256;
 
 struct PrefixChunks {
-  int q_blocks;      // row blocks of the largest set (member blocks of 16
-                     // for multi-head attention)
+  int q_blocks;      // row blocks of the largest set (member blocks of
+                     // kPrefixMembersPerWorkgroup for multi-head attention)
   int chunk_tokens;
   int n_chunks;
 };
 
 // Multi-head attention (one query head per KV head) takes its prefix on
-// the grouped-query decode kernel's structure: 16 members of a set are the
-// columns of the products, the four wavefronts split the whole prefix, and
-// one partial per (member, head) comes out: a few MB where the chunked
-// products would write one per chunk.  Grouped-query attention fills the
+// the grouped-query decode kernel's structure: 32 members of a set are the
+// columns of the products (two 16-column tiles against every tile loaded),
+// the four wavefronts split the prefix (or one chunk of it), and one
+// partial per (member, head, chunk) comes out: a few MB where the 128-token
+// chunks of the chunked products would write several times as much.  Grouped-query attention fills the
 // columns with a member's heads instead, so it takes the chunked products,
 // whose 128-row blocks read each chunk once for 128 / G members.
 bool prefix_by_members(const pkv_dims *d) { return d->num_heads == d->num_kv_heads; }
@@ -375,10 +376,11 @@ int prefix_chunks(const pkv_dims *d, const pkv_prefix_info *info, PrefixChunks *
   if (prefix_by_members(d)) {
     // chunks (of at least 256 tokens) only when the (set, head, member
     // block) units leave compute units idle: each chunk adds a partial per
-    // (member, head), and more workgroups reading one head's tiles slow
-    // each other down (128 members x 32 heads over 1024 tokens: one chunk
-    // 16.6 us, two 17.4, four 22.3, then the decode 91.0 / 91.3 / 92.5 us)
-    pc->q_blocks = (info->max_members + 15) / 16;
+    // (member, head).  128 members x 32 heads over 1024 tokens, 32 members
+    // per workgroup: one chunk 18.6 us, two 14.9 us (decode 90.7 / 90.9
+    // us); 16 members per workgroup: one chunk 16.1 us, two 17.4, four 22.3
+    pc->q_blocks = (info->max_members + pkv::kPrefixMembersPerWorkgroup - 1) /
+                   pkv::kPrefixMembersPerWorkgroup;
     const int64_t base = (int64_t)info->num_groups * d->num_kv_heads * pc->q_blocks;
     const int64_t tok = info->max_prefix_tokens;
     int64_t n = base > 0 ? (kPrefixMemberTarget + base - 1) / base : 1;

@@ -58,8 +58,9 @@ __device__ __forceinline__ uint32_t from_other_half(uint32_t old, uint32_t src) 
 
 // QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3)
 // PFX: the shared-prefix partials of multi-head attention instead (below):
-// the 16 columns are up to 16 members of a sharer set, all with query head
-// g = KV head g, walking the set's prefix.
+// the columns are up to 16 * kPrefixColTiles members of a sharer set, all
+// with query head g = KV head g, walking a chunk of the set's prefix; each
+// loaded tile meets every 16-column tile of them.
 template <int QT, int CT, int D, int BS, bool SPLIT, bool PFX = false>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_mfma_kernel(DecodeArgs a) {
@@ -70,6 +71,8 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int KC = D / 32;          // logit MFMAs per tile
   constexpr int NT = D / 16;          // value n-tiles
   constexpr bool KW = F8 && D == 128; // K loaded as whole rows, then exchanged
+  // 16-column tiles of the products (members, for prefix partials)
+  constexpr int MCT = PFX ? kPrefixColTiles : 1;
 
   static_assert(!(PFX && SPLIT), "prefix partials run single-pass");
   const int g = blockIdx.x;
@@ -79,8 +82,8 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // LDS: the merge of the 4 wavefronts; before the loop it holds the length
   // histogram of the longest-first order
-  __shared__ float sm_o[kDecodeWaves][16][D + 4];
-  __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
+  __shared__ float sm_o[kDecodeWaves][16 * MCT][D + 4];
+  __shared__ float sm_m[kDecodeWaves][16 * MCT], sm_l[kDecodeWaves][16 * MCT];
   static_assert(sizeof(sm_o) >= kOrderScratchInts * sizeof(int), "order scratch");
   // prefix partials: set gi, its members mcol0 .. mcol0 + ncol - 1 as the
   // columns; the set's first member's table is walked over its prefix
@@ -98,9 +101,9 @@ decode_mfma_kernel(DecodeArgs a) {
     members = gtok + a.num_groups;
     const int m0 = min(max(starts[gi], 0), a.num_members);
     const int m1 = min(max(starts[gi + 1], m0), a.num_members);
-    mcol0 = m0 + mb * 16;
+    mcol0 = m0 + mb * 16 * MCT;
     if (mcol0 >= m1) return;  // the whole workgroup
-    ncol = min(16, m1 - mcol0);
+    ncol = min(16 * MCT, m1 - mcol0);
     s = min(max(members[m0], 0), a.num_seqs - 1);
     ptok_set = max(0, min(gtok[gi], a.max_blocks * BS));
   } else {
@@ -162,14 +165,17 @@ decode_mfma_kernel(DecodeArgs a) {
   // Q^T operand: lane holds head `col` and the eight dims the K operand of
   // logit MFMA kk holds in this lane: (kk*4+grp)*8 for 16-bit caches,
   // 32*grp + 8*kk (D = 128) or 16*grp + 8*kk (D = 64) for 8-bit caches
-  u32x4 qop[KC];
-  {
-    const char *qp = static_cast<const char *>(a.q) + col_row(col < ncol ? col : 0) * D * 2;
+  // (column tile ct: column col + 16 ct)
+  u32x4 qop[MCT][KC];
+#pragma unroll
+  for (int ct = 0; ct < MCT; ++ct) {
+    const int c = col + 16 * ct;
+    const char *qp = static_cast<const char *>(a.q) + col_row(c < ncol ? c : 0) * D * 2;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       const int d0 = F8 ? (KW ? 32 : 16) * grp + 8 * kk : (kk * 4 + grp) * 8;
-      qop[kk] = col < ncol ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
-                           : u32x4{0u, 0u, 0u, 0u};
+      qop[ct][kk] = c < ncol ? *reinterpret_cast<const u32x4 *>(qp + d0 * 2)
+                             : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -194,17 +200,23 @@ decode_mfma_kernel(DecodeArgs a) {
   constexpr int KSTEP = KW ? 8 * D : 64;
   const uint32_t voff = (uint32_t)(grp * 4 * D * E + col * 16);
 
-  float m = -INFINITY, l = 0.f;  // head `col`; l is this lane's share
-  f32x4 acc[NT];
+  // column col + 16 ct; l is this lane's share
+  float m[MCT], l[MCT];
+  f32x4 acc[MCT][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < MCT; ++ct) {
+    m[ct] = -INFINITY;
+    l[ct] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // The wave's state to its LDS slice: head col's row sum (the four lanes'
   // shares added), maximum and weighted values; n-tile row m = 4*grp + i of
   // head col is dim 32u + 2m + j (n-tile 2u+j, 16-bit caches) or 64u + 4m + j
   // (n-tile 4u+j, 8-bit caches)
-  auto stage_state = [&]() {
-    float lt = l + __shfl_xor(l, 16);
+  auto stage_state = [&](int ct) {
+    float lt = l[ct] + __shfl_xor(l[ct], 16);
     lt += __shfl_xor(lt, 32);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -212,19 +224,19 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int mm = 4 * grp + i;
         const int d = F8 ? 64 * (nt / 4) + 4 * mm + nt % 4 : 32 * (nt / 2) + 2 * mm + nt % 2;
-        sm_o[w][col][d] = acc[nt][i];
+        sm_o[w][col + 16 * ct][d] = acc[ct][nt][i];
       }
     if (grp == 0) {
-      sm_m[w][col] = m;
-      sm_l[w][col] = lt;
+      sm_m[w][col + 16 * ct] = m[ct];
+      sm_l[w][col + 16 * ct] = lt;
     }
   };
 
 
 
   // tiles are streamed (non-temporal loads); prefix partials read each tile
-  // once per block of 16 members, all on one XCD, so there the loads keep
-  // the lines in its L2
+  // once per block of members, all on one XCD, so there the loads keep the
+  // lines in its L2
   auto load = [&](Tl &t, size_t tile_bytes) {
     const char *kp = kc + tile_bytes + koff;
     const char *vp = vc + tile_bytes + voff;
@@ -237,8 +249,10 @@ decode_mfma_kernel(DecodeArgs a) {
   };
 
   auto compute = [&](Tl &t, int n) {
-    // S^T[token 4*grp+i][head col]
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // S^T[token 4*grp+i][column col + 16 ct]
+    f32x4 sacc[MCT];
+#pragma unroll
+    for (int ct = 0; ct < MCT; ++ct) sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (F8) {
       if constexpr (KW) {
         // lanes col >= 8 take chunk 2*grp of token col from load 1 (lane
@@ -255,20 +269,25 @@ decode_mfma_kernel(DecodeArgs a) {
         const uint32_t w0 = t.k[kk / 2][2 * (kk % 2)], w1 = t.k[kk / 2][2 * (kk % 2) + 1];
         const u32x4 kop = {fp8x2_to_16<QT>(w0, false), fp8x2_to_16<QT>(w0, true),
                            fp8x2_to_16<QT>(w1, false), fp8x2_to_16<QT>(w1, true)};
-        sacc = Ops::qk(kop, qop[kk], sacc);
+#pragma unroll
+        for (int ct = 0; ct < MCT; ++ct) sacc[ct] = Ops::qk(kop, qop[ct][kk], sacc[ct]);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) sacc = Ops::qk(t.k[kk], qop[kk], sacc);
+      for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < MCT; ++ct) sacc[ct] = Ops::qk(t.k[kk], qop[ct][kk], sacc[ct]);
     }
 
     const int t0 = (tile0 + kStride * n) * 16 + 4 * grp;
     const bool tail = (tile0 + kStride * n) * 16 + 16 > tok_end;
     const int nvalid = tail ? max(0, min(4, tok_end - t0)) : 4;
-    float sc[4];
+    float sc[MCT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sc[i] = (i < nvalid && col < ncol) ? sacc[i] * a.scale_log2 : -INFINITY;
+    for (int ct = 0; ct < MCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[ct][i] = (i < nvalid && col + 16 * ct < ncol) ? sacc[ct][i] * a.scale_log2 : -INFINITY;
     if (tail) {
       // masked tokens' values may hold anything (NaN included): zero them
       if constexpr (F8) {
@@ -293,70 +312,73 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // running maximum of head `col`, shared by the 4 lanes holding it; only
-    // moved (exactly, with the cross-lane max) when a logit exceeds it by
-    // more than the slack somewhere in the wave
-    const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (wave_any(mb > m + kRescaleSlack)) {
-      float mh = fmaxf(mb, __shfl_xor(mb, 16));
-      mh = fmaxf(mh, __shfl_xor(mh, 32));
-      const float m_new = fmaxf(m, mh);
-      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));
-      l *= alpha;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
-      m = m_new;
-    }
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float p[4];
+    for (int ct = 0; ct < MCT; ++ct) {
+      // running maximum of head `col`, shared by the 4 lanes holding it; only
+      // moved (exactly, with the cross-lane max) when a logit exceeds it by
+      // more than the slack somewhere in the wave
+      const float mb = fmaxf(fmaxf(sc[ct][0], sc[ct][1]), fmaxf(sc[ct][2], sc[ct][3]));
+      if (wave_any(mb > m[ct] + kRescaleSlack)) {
+        float mh = fmaxf(mb, __shfl_xor(mb, 16));
+        mh = fmaxf(mh, __shfl_xor(mh, 32));
+        const float m_new = fmaxf(m[ct], mh);
+        const float alpha = fast_exp2(m[ct] - (m_new == -INFINITY ? 0.f : m_new));
+        l[ct] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_use);
-    if constexpr (F8) {
-      // values with 4 significant bits: one probability operand rounded to
-      // the 16-bit type (8 or 11 bits) is ample, and the sum adds exactly
-      // the rounded weights
-      float r0, r1, r2, r3;
-      const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
-      l += (r0 + r1) + (r2 + r3);
-      // chunk u, word j: the four tokens of dim 64u + 4*col + j -> n-tile 4u+j
-#pragma unroll
-      for (int u = 0; u < Tl::NC; ++u) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2 va = {fp8x2_to_16<QT>(t.v[u][j], false), fp8x2_to_16<QT>(t.v[u][j], true)};
-          acc[4 * u + j] = Ops::pv(va, pr, acc[4 * u + j]);
-        }
+        for (int nt = 0; nt < NT; ++nt) acc[ct][nt] *= alpha;
+        m[ct] = m_new;
       }
-    } else if constexpr (PFX) {
-      // prefix partials: one probability operand rounded to the 16-bit
-      // type, the sum over exactly the rounded weights (the precision of
-      // the chunked-prefill products); half the value products
-      float r0, r1, r2, r3;
-      const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
-      l += (r0 + r1) + (r2 + r3);
+      const float m_use = m[ct] == -INFINITY ? 0.f : m[ct];
+      float p[4];
 #pragma unroll
-      for (int u = 0; u < Tl::NC; ++u) {
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[ct][i] - m_use);
+      if constexpr (F8) {
+        // values with 4 significant bits: one probability operand rounded to
+        // the 16-bit type (8 or 11 bits) is ample, and the sum adds exactly
+        // the rounded weights
+        float r0, r1, r2, r3;
+        const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
+        l[ct] += (r0 + r1) + (r2 + r3);
+        // chunk u, word j: the four tokens of dim 64u + 4*col + j -> n-tile 4u+j
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
-          acc[2 * u + j] = Ops::pv(va, pr, acc[2 * u + j]);
+        for (int u = 0; u < Tl::NC; ++u) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x2 va = {fp8x2_to_16<QT>(t.v[u][j], false), fp8x2_to_16<QT>(t.v[u][j], true)};
+            acc[ct][4 * u + j] = Ops::pv(va, pr, acc[ct][4 * u + j]);
+          }
         }
-      }
-    } else {
-      l += (p[0] + p[1]) + (p[2] + p[3]);
-      uint32_t h01, l01, h23, l23;
-      Ops::split2(p[0], p[1], h01, l01);
-      Ops::split2(p[2], p[3], h23, l23);
-      const u32x2 phi = {h01, h23};
-      const u32x2 plo = {l01, l23};
-      // chunk u, words 2j..2j+1: the four tokens of dim 32u + 2*col + j
+      } else if constexpr (PFX) {
+        // prefix partials: one probability operand rounded to the 16-bit
+        // type, the sum over exactly the rounded weights (the precision of
+        // the chunked-prefill products); half the value products
+        float r0, r1, r2, r3;
+        const u32x2 pr = {Ops::round2(p[0], p[1], r0, r1), Ops::round2(p[2], p[3], r2, r3)};
+        l[ct] += (r0 + r1) + (r2 + r3);
 #pragma unroll
-      for (int u = 0; u < Tl::NC; ++u) {
+        for (int u = 0; u < Tl::NC; ++u) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
-          acc[2 * u + j] = Ops::pv(va, phi, acc[2 * u + j]);
-          acc[2 * u + j] = Ops::pv(va, plo, acc[2 * u + j]);
+          for (int j = 0; j < 2; ++j) {
+            const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
+            acc[ct][2 * u + j] = Ops::pv(va, pr, acc[ct][2 * u + j]);
+          }
+        }
+      } else {
+        l[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+        uint32_t h01, l01, h23, l23;
+        Ops::split2(p[0], p[1], h01, l01);
+        Ops::split2(p[2], p[3], h23, l23);
+        const u32x2 phi = {h01, h23};
+        const u32x2 plo = {l01, l23};
+        // chunk u, words 2j..2j+1: the four tokens of dim 32u + 2*col + j
+#pragma unroll
+        for (int u = 0; u < Tl::NC; ++u) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const u32x2 va = {t.v[u][2 * j], t.v[u][2 * j + 1]};
+            acc[ct][2 * u + j] = Ops::pv(va, phi, acc[ct][2 * u + j]);
+            acc[ct][2 * u + j] = Ops::pv(va, plo, acc[ct][2 * u + j]);
+          }
         }
       }
     }
@@ -376,7 +398,7 @@ decode_mfma_kernel(DecodeArgs a) {
                         load, compute);
   }
 
-  stage_state();
+  if constexpr (!PFX) stage_state(0);
   if constexpr (SPLIT) {
     // the wave's partial, row by row from its own LDS slice (written and
     // read by this wave only: ordering inside the wave is all it needs),
@@ -400,6 +422,8 @@ decode_mfma_kernel(DecodeArgs a) {
   if constexpr (PFX) {
     // ---- merge the 4 wavefronts into each member's partial: maximum,
     //      sum of weights and un-normalised weighted values ----
+#pragma unroll
+    for (int ct = 0; ct < MCT; ++ct) stage_state(ct);
     __syncthreads();
     for (int idx = tid; idx < ncol * D; idx += kDecodeThreads) {
       const int hh = idx / D, d = idx % D;

@@ -15,6 +15,10 @@ constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = 4;
 // Most partitions one wave of the vector kernel's split launch computes.
 constexpr int kMaxPartsPerWave = 4;
+// Multi-head shared-prefix partials: blocks of 16 members (matrix-core
+// columns) one workgroup computes against each prefix tile it loads.
+constexpr int kPrefixColTiles = 2;
+constexpr int kPrefixMembersPerWorkgroup = 16 * kPrefixColTiles;
 
 // Compute units of the current device (256 if the query fails; a failed
 // query's error is cleared so that it cannot read as a failed launch).
@@ -82,8 +86,9 @@ struct DecodeArgs {
   int n_pchunks;
   // shared-prefix partials on the grouped-query kernel's structure (one
   // KV head per query head): the plan of pkv_prefix_plan, its set count,
-  // member count and member blocks of 16 per set; the partials go to ws_*
-  // ([S, Hq] rows, one chunk covering the whole prefix)
+  // member count and member blocks (kPrefixMembersPerWorkgroup) per set;
+  // the partials go to ws_* ([S, Hq, n_pchunks] rows, one per chunk of
+  // pchunk_tokens)
   const int32_t *plan;
   int num_groups;
   int num_members;
@@ -180,9 +185,9 @@ int64_t prefill_grid(int num_seqs, int num_kv_heads, int q_blocks);
 hipError_t launch_prefix_mfma(const PrefillArgs &a, int dtype, int cache_dtype,
                               int head_dim, int block_size, hipStream_t st);
 // Shared-prefix partials for multi-head attention: one workgroup per
-// (KV head, set, block of 16 members) walks the whole prefix, its four
-// wavefronts splitting the tiles, and writes one partial per (member,
-// head).
+// (KV head, set and block of kPrefixMembersPerWorkgroup members, chunk)
+// walks the chunk, its four wavefronts splitting the tiles, and writes one
+// partial per (member, head, chunk).
 hipError_t launch_prefix_mha(const DecodeArgs &a, int dtype, int head_dim,
                              int block_size, hipStream_t st);
 int64_t prefix_grid(int num_groups, int num_kv_heads, int n_chunks, int q_blocks);
