@@ -98,6 +98,7 @@ CASES = [
     (5, 40, 2, 2, 128, 32, "bf16", 1, 70, 64),      # long prefix, short suffix
     (6, 9, 64, 8, 128, 16, "bf16", 1, 20, 100),     # 70B-class heads
     (7, 150, 16, 16, 128, 16, "f16", 2, 8, 40),     # more members than a row block
+    (8, 46, 8, 8, 128, 16, "bf16", 2, 20, 100),     # 22 members: a part-filled second column tile
 ]
 
 
