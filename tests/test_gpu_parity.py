@@ -278,6 +278,26 @@ def test_very_wide_block_table():
     compare(to_f64(dev.decode(kd, vd)), want, "bf16", "wide table")
 
 
+@pytest.mark.parametrize("S", [1024, 1025, 65535])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 2)])
+def test_many_sequences(S, Hq, Hkv):
+    """Up to the most sequences a call takes (65535, the grid limit), short
+    ragged contexts with empty ones among them, on both decode kernels,
+    single pass and split: every output against the oracle.  1024 and 1025
+    sit on either side of the longest-first order's limit."""
+    w = wl.random_case(9400 + S + Hq, num_seqs=S, max_len=40, num_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=64, block_size=16, dtype="bf16",
+                       pool_factor=1.3)
+    print(f"[{S} sequences] Hq={Hq} Hkv={Hkv} D=64 bf16", flush=True)
+    kc, vc = oracle_pool(w)
+    want = oracle_out(w, kc, vc)
+    dev = Dev(w)
+    kd, vd = dev.cache_from_host(kc, vc)
+    for variant in ("single", "split"):
+        got = to_f64(dev.decode(kd, vd, variant=variant, partition=16))
+        compare(got, want, "bf16", f"{S} sequences {variant}")
+
+
 @pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 8, 2), ("f16", 2, 2)])
 def test_quarter_million_token_contexts(dtype, Hq, Hkv):
     """Contexts of 262144 and 200001 tokens (16384 and 12501 blocks of 16),
