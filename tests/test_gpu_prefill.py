@@ -169,6 +169,35 @@ def test_full_size_sampled(name):
     compare(got[sel[:, 0], sel[:, 1]], want, w.dtype, name)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 16, 2), ("f16", 4, 4)])
+def test_long_chunks_sampled(dtype, Hq, Hkv):
+    """Long chunks: 8192 tokens after a 24576-token context, and a whole
+    9001-token prompt as one chunk (grouped-query on 128-row blocks of 16
+    tokens x 8 heads; multi-head on 128 tokens).  Sampled (token, head)
+    pairs against the oracle, the first and last tokens of each chunk and
+    the block edges of the 128-row blocks among them."""
+    w = wl.build("longchunk", lens=[32768, 9001], num_heads=Hq, num_kv_heads=Hkv,
+                 head_dim=128, block_size=16, dtype=dtype, seed=8800 + Hq,
+                 pool_factor=1.2, chunk_lens=[8192, 9001])
+    print_case("prefill-long", w)
+    out, kc, vc = gpu_step(w)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    kh, vh = oracle_state(w)
+    T = w.q.shape[0]
+    G = Hq // Hkv
+    rng = np.random.default_rng(6)
+    edges = np.arange(0, T, max(1, 128 // G))
+    rows = np.concatenate([w.query_start_loc[:-1], w.query_start_loc[1:] - 1,
+                           edges[::7], np.maximum(edges[::7] - 1, 0),
+                           rng.integers(0, T, 64)])
+    sel = np.stack([rows, rng.integers(0, Hq, rows.size)], 1).astype(np.int32)
+    want = oracle.paged_prefill(w.q, kh, vh, w.block_tables, w.context_lens,
+                                w.query_start_loc, w.scale, w.block_size,
+                                w.num_kv_heads, w.num_blocks, w.dtype, sel=sel)
+    compare(got[sel[:, 0], sel[:, 1]], want, w.dtype, "long chunks")
+
+
 FP8_CASES = [
     # dtype, bs, Hq, Hkv, D, S, max_prior, max_chunk, k_scale, v_scale
     ("bf16", 16, 8, 2, 128, 4, 200, 60, 0.05, 0.5),
