@@ -543,6 +543,23 @@ def reduce_counters(root):
                      f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
         L.append("")
+        # the launches of the bench's last timed pass (the event-timed one in
+        # the decode and prefill modes): the last `steps` of each kernel in
+        # the trace, so that the clock ramp of the first launches stays out
+        trace_path = _find(os.path.join(d, "kt"), "kernel_trace.csv")
+        last_us = None
+        if trace_path and "steps" in rec:
+            trace = list(csv.DictReader(open(trace_path)))
+            steps = int(rec["steps"])
+            last_us = 0.0
+            for k in kernels:
+                rows = sorted((r for r in trace if k in r["Kernel_Name"]),
+                              key=lambda r: int(r["Start_Timestamp"]))[-steps:]
+                last_us += sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                               for r in rows) / len(rows) / 1e3
+            L += [f"Kernel-trace mean of the last {steps} launches of `{kernel}` (the "
+                  f"bench's last timed pass, each kernel's mean added for a two-launch "
+                  f"attention): {last_us:.1f} us.", ""]
         if any("reshape_and_cache" in r["Name"] for r in stats):
             L += ["The reshape_and_cache average includes the one large call that "
                   "fills the earlier context; the per-step calls are the minimum.", ""]
@@ -551,7 +568,11 @@ def reduce_counters(root):
         L.append(f"bench.py in the same run (HIP events on the launch stream): mean "
                  f"launch {mean_us:.1f} us, roofline {roof['achieved']:.0f} {unit} = "
                  f"{100*roof['frac']:.1f}% of {roof['peak']:.0f} {unit}, step "
-                 f"{rec['ms_per_step']*1e3:.1f} us.")
+                 f"{rec['ms_per_step']*1e3:.1f} us." + (
+                     f" The events add the launch gaps to the kernel time "
+                     f"({100 * (mean_us / last_us - 1):+.1f}% against the trace mean "
+                     f"above); the table's averages also hold the warm-up launches, the "
+                     f"first of them at rising clocks." if last_us else ""))
         L += ["", "HBM traffic per launch, from two counter passes:", "", "```",
               pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE"), "```", ""]
         f = _counter(os.path.join(d, "FETCH_SIZE"), "FETCH_SIZE")

@@ -106,7 +106,7 @@ def test_reduce_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     (d / "FETCH_SIZE").mkdir()
     (d / "WRITE_SIZE").mkdir()
     (d / "args.txt").write_text("--workload long_split --variant split")
-    rec = {"metric": "m", "ms_per_step": 0.7, "dtype": "bf16",
+    rec = {"metric": "m", "ms_per_step": 0.7, "dtype": "bf16", "steps": 50,
            "config": {"workload": "long_split"},
            "roofline": {"kernel": "decode_vector_kernel + partition_reduce_kernel",
                         "mean_launch_ms": 0.68, "achieved": 6300.0, "frac": 0.79,
@@ -117,6 +117,19 @@ def test_reduce_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
         '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
         '"void pkv::decode_vector_kernel<2, 2, 128, 16, true, false>(pkv::DecodeArgs)",'
         '50,33000000,660000,97.0,650000,700000,1000\n')
+
+    # a trace of 60 partial-kernel launches, the first ten slow (clock ramp),
+    # and 60 reduce launches: the bench's last timed pass is the last 50
+    vk_name = "void pkv::decode_vector_kernel<2, 2, 128, 16, true, false>(pkv::DecodeArgs)"
+    rows = ['"Kernel_Name","Start_Timestamp","End_Timestamp"']
+    t0 = 1000
+    for i in range(60):
+        dur = 700000 if i < 10 else 650000
+        rows.append(f'"{vk_name}",{t0},{t0 + dur}')
+        rows.append(f'"void pkv::partition_reduce_kernel<2, 128>(pkv::DecodeArgs)",'
+                    f'{t0 + dur + 100},{t0 + dur + 5100}')
+        t0 += dur + 10000
+    (d / "kt" / "run_kernel_trace.csv").write_text("\n".join(rows) + "\n")
 
     def passes(counter, kern_vals, copy_val):
         rows = ["Kernel_Name,Counter_Name,Counter_Value"]
@@ -143,3 +156,5 @@ def test_reduce_counters_scales_by_the_calibration_copy(tmp_path, monkeypatch):
         "decode_vector_kernel+partition_reduce_kernel")
     md = (prof / "decode_vector_kernel+partition_reduce_kernel_long_split.md").read_text()
     assert "--workload long_split --variant split" in md and "| 50 | 660.0 |" in md
+    # the trace mean of the last 50 launches of each kernel, added: 650 + 5 us
+    assert "the last 50 launches" in md and "attention): 655.0 us." in md
