@@ -21,8 +21,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - All data pointers are DEVICE pointers (HBM), owned by the caller.  The
- *   library allocates nothing, keeps no mutable state and may be called from
- *   several host threads.
+ *   library allocates nothing and may be called from several host threads;
+ *   the one state it keeps is the static scratch of
+ *   paged_attention_decode_split_static (one array per device, its address
+ *   looked up once per device).
  * - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
  *   NULL means the default stream) and the call returns before it runs.
  * - One element type covers q, out, k, v and both caches (pkv_dims.dtype).
