@@ -161,51 +161,33 @@ __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
-// Longest-first order of the single-pass grid.  Work items of one launch
-// differ in length by up to two orders of magnitude; the dispatcher starts
-// workgroups in grid order, so a long sequence that starts late stretches
-// the end of the kernel.  Workgroup row r therefore processes the sequence
-// of rank r in an order of decreasing context length, computed in every
-// workgroup from context_lens with a counting select:
-//   * lengths (clamped to [0, max_tokens]) fall into 256 buckets of equal
-//     width 2^sh, bucket (max_tokens - L) >> sh, so bucket 0 holds the
-//     longest;
+// Counting select: the item of rank r (0 <= r < n) when items 0 .. n-1 are
+// ordered by bucket(i) in [0, kOrderBuckets), ascending, and by index within
+// a bucket.  Computed in every workgroup that needs it:
 //   * a histogram of the buckets in LDS and its prefix sum give the bucket
 //     that holds rank r and r's place k inside it;
-//   * the k-th sequence of that bucket in sequence order is the result.
-// The order is longest-first up to the bucket width (max_tokens / 256
-// tokens or less).  Each thread does O(S / 256 + 1) work.  `scratch` is LDS
-// of at least kOrderScratchInts ints, free for reuse once this returns; the
-// result only chooses which workgroup does which sequence, never the
-// arithmetic.
+//   * the k-th item of that bucket in index order is the result.
+// Each thread does O(n / NT + 1) work and calls bucket() at most twice per
+// item (item i in pass p by thread i % NT).  `scratch` is LDS of at least
+// kOrderScratchInts ints, free for reuse once this returns; the select takes
+// no other LDS (in a kernel whose LDS sits at the limit for two workgroups
+// per CU, a few more bytes halve the occupancy).  Called by every thread of
+// the workgroup.
 constexpr int kOrderBuckets = 256;
 constexpr int kOrderScratchInts = kOrderBuckets + 8;
-// Every workgroup reads all S lengths to find its rank, so the order costs
-// O(S) per workgroup.  Above this many sequences the grid keeps sequence
-// order: its cost outgrows the tail it saves (short contexts, bf16, 2 or 8
-// heads: 2048 sequences 26.6 -> 15.5 us, 4096 62 -> 22 us, 16384 544 -> 74
-// us; 1024 sequences alike either way).
-constexpr int kOrderMaxSeqs = 1024;
 
-template <int NT>
-__device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, int S,
-                                                 int max_tokens, int r, int *scratch) {
+template <int NT, class Bucket>
+__device__ __forceinline__ int counting_select(int n, int r, const Bucket &bucket,
+                                               int *scratch) {
   static_assert(NT == kOrderBuckets, "one thread per bucket");
-  __shared__ int sel_bucket, sel_k, chosen;
   int *hist = scratch;                  // kOrderBuckets counters
   int *wsum = scratch + kOrderBuckets;  // one total per wavefront
-  if (S > kOrderMaxSeqs) return r;  // uniform over the workgroup
+  int &sel_bucket = scratch[kOrderBuckets + 4], &sel_k = scratch[kOrderBuckets + 5];
+  int &chosen = scratch[kOrderBuckets + 6];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  max_tokens = max(max_tokens, 0);
-  int sh = 0;
-  while ((max_tokens >> sh) >= kOrderBuckets) ++sh;
-  auto bucket = [&](int i) {
-    const int L = max(0, min(context_lens[i], max_tokens));
-    return (max_tokens - L) >> sh;
-  };
   hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < S; i += NT) atomicAdd(&hist[bucket(i)], 1);
+  for (int i = tid; i < n; i += NT) atomicAdd(&hist[bucket(i)], 1);
   __syncthreads();
   // inclusive prefix sum of the histogram: within each wavefront, then the
   // totals of the wavefronts before it
@@ -219,17 +201,17 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
   if (lane == 63) wsum[w] = x;
   __syncthreads();
   for (int q = 0; q < w; ++q) x += wsum[q];
-  if (x - h <= r && r < x) {  // exactly one bucket holds rank r (r < S)
+  if (x - h <= r && r < x) {  // exactly one bucket holds rank r (r < n)
     sel_bucket = tid;
     sel_k = r - (x - h);
   }
   __syncthreads();
   const int bsel = sel_bucket, k = sel_k;
-  // the k-th member of bucket bsel in sequence order, NT sequences a pass
+  // the k-th member of bucket bsel in index order, NT items a pass
   int base = 0;
-  for (int c = 0; c < S; c += NT) {
+  for (int c = 0; c < n; c += NT) {
     const int i = c + tid;
-    const bool f = i < S && bucket(i) == bsel;
+    const bool f = i < n && bucket(i) == bsel;
     const uint64_t bal = __builtin_amdgcn_ballot_w64(f);
     const int before_lane = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wsum[w] = __builtin_popcountll(bal);
@@ -244,7 +226,40 @@ __device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, in
     __syncthreads();  // wsum is rewritten by the next pass
     if (base > k) break;  // uniform: every thread holds the same base
   }
-  return chosen;
+  const int result = chosen;
+  __syncthreads();  // the scratch is the caller's again
+  return result;
+}
+
+// Longest-first order of the single-pass grid.  Work items of one launch
+// differ in length by up to two orders of magnitude; the dispatcher starts
+// workgroups in grid order, so a long sequence that starts late stretches
+// the end of the kernel.  Workgroup row r therefore processes the sequence
+// of rank r in an order of decreasing context length, a counting select
+// over context_lens: lengths (clamped to [0, max_tokens]) fall into 256
+// buckets of equal width 2^sh, bucket (max_tokens - L) >> sh, so bucket 0
+// holds the longest.  The order is longest-first up to the bucket width
+// (max_tokens / 256 tokens or less); it only chooses which workgroup does
+// which sequence, never the arithmetic.
+// Every workgroup reads all S lengths to find its rank, so the order costs
+// O(S) per workgroup.  Above this many sequences the grid keeps sequence
+// order: its cost outgrows the tail it saves (short contexts, bf16, 2 or 8
+// heads: 2048 sequences 26.6 -> 15.5 us, 4096 62 -> 22 us, 16384 544 -> 74
+// us; 1024 sequences alike either way).
+constexpr int kOrderMaxSeqs = 1024;
+
+template <int NT>
+__device__ __forceinline__ int longest_first_seq(const int32_t *context_lens, int S,
+                                                 int max_tokens, int r, int *scratch) {
+  if (S > kOrderMaxSeqs) return r;  // uniform over the workgroup
+  max_tokens = max(max_tokens, 0);
+  int sh = 0;
+  while ((max_tokens >> sh) >= kOrderBuckets) ++sh;
+  const auto bucket = [&](int i) {
+    const int L = max(0, min(context_lens[i], max_tokens));
+    return (max_tokens - L) >> sh;
+  };
+  return counting_select<NT>(S, r, bucket, scratch);
 }
 
 // Leading blocks of a context of tok_end tokens that the neighbouring

@@ -43,9 +43,13 @@
 // token rows use different banks.
 //
 // Scheduling: workgroup i runs on XCD i % 8.  All row blocks of one
-// (sequence, KV head) are given consecutive workgroup numbers on one XCD,
+// (sequence, KV head) belong to one XCD and are numbered consecutively,
 // latest rows (longest prefixes) first, so the sequence's K/V stay in that
-// XCD's L2 while its row blocks run.
+// XCD's L2 while its row blocks run.  A grid of at most 256 row blocks per
+// XCD runs them longest walk first instead (ties in that order): the
+// dispatcher starts workgroups in grid order, and with two or three row
+// blocks per workgroup slot a long one that starts late sets the end of the
+// launch.
 //
 // 8-bit caches: the ring holds the 1-byte codes (half the bytes per stage).
 // A 16-byte K read gives 16 dims of one token, widened exactly to the
@@ -74,6 +78,14 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillNQ = 2;  // 16-row query tiles per wavefront
 constexpr int kPrefillRows = kPrefillWaves * kPrefillNQ * 16;
 constexpr int kXcds = 8;
+// Above this many row blocks per XCD the grid keeps its plain order: the
+// longest-first order costs every workgroup a select over all of its XCD's
+// row blocks (about 2 us), and with many row blocks per slot the tail it
+// saves is a small part of the launch.  Measured: 160 per XCD (13B-class
+// prefill, 8 chunks of 512 tokens x 40 heads) 99.9 -> 92.5 us, E4M3 caches
+// 98.2 -> 84.9 us; 512 per XCD (70B-class) 530 -> 550 us with the order (a
+// select over two row blocks per thread), 525 us with a precomputed order.
+constexpr int kPrefillOrderMaxUnits = 256;
 
 int prefill_rows_per_workgroup() { return kPrefillRows; }
 
@@ -140,7 +152,8 @@ __device__ __forceinline__ void wait_vm() {
 
 // QT: element type of q and out (16-bit); CT: of the caches (QT or E4M3).
 // PREFIX: the shared-prefix partials instead of chunked prefill (below).
-template <int QT, int CT, int D, int BS, bool PREFIX = false>
+// ORDER (prefill): the row blocks of each XCD in longest-first order (below).
+template <int QT, int CT, int D, int BS, bool PREFIX = false, bool ORDER = false>
 __global__ void __launch_bounds__(kPrefillThreads)
 prefill_mfma_kernel(PrefillArgs a) {
   using Ops = MfmaOps<QT>;
@@ -157,8 +170,44 @@ prefill_mfma_kernel(PrefillArgs a) {
 
   const int Hkv = a.num_kv_heads, Hq = a.num_heads;
   const int G = Hq / Hkv;
-  const int wgi = blockIdx.x;
-  const int xcd = wgi % kXcds, nth = wgi / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  int nth = blockIdx.x / kXcds;
+  if constexpr (ORDER) {
+    // Longest-first order of this XCD's row blocks.  The dispatcher starts
+    // workgroups in grid order, and a row block's walk ranges from a few
+    // super-tiles to the whole context; a long one that starts late
+    // stretches the end of the launch.  Rank nth of the XCD therefore takes
+    // the XCD-local row block of rank nth in an order of decreasing walk
+    // (ties in grid order, which keeps a pair's row blocks together): a
+    // counting select over the walks in super-tiles, 256 buckets of width
+    // 2^sh, one row block per thread, each walk computed as below.
+    static_assert(!PREFIX, "prefill only");
+    static_assert(kPrefillOrderMaxUnits <= kPrefillThreads, "one row block per thread");
+    static_assert(sizeof(ring) >= kOrderScratchInts * sizeof(int), "order scratch");
+    const int units = gridDim.x / kXcds;  // <= kPrefillOrderMaxUnits (the host checks)
+    const int max_tok = a.max_blocks * BS;
+    const int max_work = (max_tok + 31) >> 5;
+    int sh = 0;
+    while ((max_work >> sh) >= kOrderBuckets) ++sh;
+    // row block j = threadIdx.x (its three loads issued at once)
+    const int j = threadIdx.x;
+    const int pr = (j / a.q_blocks) * kXcds + xcd;
+    const int sq = min(pr / Hkv, a.num_seqs - 1);
+    const int T = a.num_query_tokens;
+    const int c0 = min(max(a.query_start_loc[sq], 0), T);
+    const int c1 = min(max(a.query_start_loc[sq + 1], c0), T);
+    const int Cs = c1 - c0, Ls = max(0, min(a.context_lens[sq], max_tok));
+    const int r0 = (a.q_blocks - 1 - j % a.q_blocks) * kPrefillRows;
+    int work = 0;
+    if (j < units && pr < a.num_seqs * Hkv && r0 < Cs * G) {
+      const int kv_end = min(Ls, Ls - Cs + (min(r0 + kPrefillRows, Cs * G) - 1) / G + 1);
+      work = kv_end > 0 ? (kv_end + 31) >> 5 : 0;
+    }
+    const int my_bucket = (max_work - work) >> sh;
+    // with units <= threads, item i of both passes is thread i's
+    nth = counting_select<kPrefillThreads>(
+        units, nth, [&](int) { return my_bucket; }, reinterpret_cast<int *>(ring));
+  }
   const int pair = (nth / a.q_blocks) * kXcds + xcd;
   const int blk = a.q_blocks - 1 - nth % a.q_blocks;
 
@@ -620,7 +669,10 @@ prefill_mfma_kernel(PrefillArgs a) {
   // normalise and store: row m = 4*grp + i of n-tile 2u+j is dim
   // 32u + 16j + m of the lane's query row (16-bit caches), of n-tile 4u+j
   // dim 64u + 4m + j (8-bit caches); either way the lane holds four
-  // adjacent dims, stored as one 64-bit word
+  // adjacent dims, stored as one 64-bit word.  Each pair is rounded to the
+  // 16-bit type (nearest even) by one packed conversion: the outputs are
+  // finite, and the bit-level rounding with its NaN branch took more than
+  // twice the instructions of the whole bfloat16 epilogue.
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const float lt = lsum[qt][0];
@@ -633,20 +685,16 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = 64 * u + 4 * (4 * grp + i);
-          const u32x2 wv = {from_f32<QT>(acc[qt][4 * u][i] * inv) |
-                                (from_f32<QT>(acc[qt][4 * u + 1][i] * inv) << 16),
-                            from_f32<QT>(acc[qt][4 * u + 2][i] * inv) |
-                                (from_f32<QT>(acc[qt][4 * u + 3][i] * inv) << 16)};
+          const u32x2 wv = {Ops::pack2(acc[qt][4 * u][i] * inv, acc[qt][4 * u + 1][i] * inv),
+                            Ops::pack2(acc[qt][4 * u + 2][i] * inv, acc[qt][4 * u + 3][i] * inv)};
           *reinterpret_cast<u32x2 *>(op + (d >> 1)) = wv;
         }
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int d = 32 * (t / 2) + 16 * (t % 2) + 4 * grp;
-        const u32x2 wv = {from_f32<QT>(acc[qt][t][0] * inv) |
-                              (from_f32<QT>(acc[qt][t][1] * inv) << 16),
-                          from_f32<QT>(acc[qt][t][2] * inv) |
-                              (from_f32<QT>(acc[qt][t][3] * inv) << 16)};
+        const u32x2 wv = {Ops::pack2(acc[qt][t][0] * inv, acc[qt][t][1] * inv),
+                          Ops::pack2(acc[qt][t][2] * inv, acc[qt][t][3] * inv)};
         *reinterpret_cast<u32x2 *>(op + (d >> 1)) = wv;
       }
     }
@@ -687,8 +735,14 @@ hipError_t launch_prefix_mfma(const PrefillArgs &a, int dtype, int cache_dtype, 
 template <int QT, int CT, int D, int BS>
 static hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st) {
   const int64_t n = prefill_grid(a.num_seqs, a.num_kv_heads, a.q_blocks);
-  hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS>), dim3((unsigned)n),
-                     dim3(kPrefillThreads), 0, st, a);
+  // a kernel of its own for the ordered grid: the select, inlined into the
+  // other, changed the register allocation of its main loop (2% slower)
+  if (n / kXcds <= kPrefillOrderMaxUnits)
+    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS, false, true>), dim3((unsigned)n),
+                       dim3(kPrefillThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<QT, CT, D, BS>), dim3((unsigned)n),
+                       dim3(kPrefillThreads), 0, st, a);
   return hipGetLastError();
 }
 

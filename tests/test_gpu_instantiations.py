@@ -115,3 +115,42 @@ def test_prefill_instantiation(dt, cache, D, bs):
     got = to_f64(out)
     assert np.all(np.isfinite(got))
     compare(got, want, dt, f"prefill {dt} {cache} D={D} bs={bs}")
+
+
+PLAIN = list(itertools.product(("f16", "bf16"), ("same", "fp8"), (64, 128), (16, 32)))
+
+
+@pytest.mark.parametrize("dt,cache,D,bs", PLAIN)
+def test_prefill_instantiation_plain_grid(dt, cache, D, bs):
+    """The matrix-core prefill has a second instantiation for grids of more
+    than 256 row blocks per XCD, which keep the grid order (the sweep above
+    runs the longest-first one).  Many short chunks with max_query_len left
+    at its default (all query tokens) give such a grid: about 300 sequences
+    x 2 KV heads x 38 row blocks, most of them past their sequence's rows."""
+    import paged_kv_cache_309_amd as pkv
+    Hkv, G = 2, 2
+    seed = 7600 + PLAIN.index((dt, cache, D, bs))
+    w = wl.random_prefill_case(seed, num_seqs=300, max_prior=60, max_chunk=16,
+                               num_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                               block_size=bs, dtype=dt, pool_factor=1.5)
+    T = int(w.query_start_loc[-1])
+    row_blocks = -(-T * G // 128)
+    grid = 8 * -(-(w.num_seqs * Hkv) // 8) * row_blocks
+    assert grid // 8 > 256, grid
+    print(f"[inst prefill plain] {dt} cache={cache} D={D} bs={bs} T={T} grid={grid}",
+          flush=True)
+    kc, vc, kd, vd = _pools(w, cache)
+    q = to_torch(w.q, dt)
+    out = torch.empty_like(q)
+    pkv.paged_attention_prefill(out, q, kd, vd, torch.from_numpy(w.block_tables).cuda(),
+                                torch.from_numpy(w.context_lens).cuda(),
+                                torch.from_numpy(w.query_start_loc).cuda(), w.scale,
+                                **_scales(cache))
+    torch.cuda.synchronize()
+    want = oracle.paged_prefill(w.q, kc, vc, w.block_tables, w.context_lens,
+                                w.query_start_loc, w.scale, bs, Hkv, w.num_blocks, dt,
+                                cache_dtype="fp8" if cache == "fp8" else None,
+                                **_scales(cache))
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    compare(got, want, dt, f"prefill plain grid {dt} {cache} D={D} bs={bs}")
