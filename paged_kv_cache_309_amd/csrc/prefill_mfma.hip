@@ -42,14 +42,17 @@
 // 16-byte chunks permuted (see PrefillRing) so that lanes reading different
 // token rows use different banks.
 //
-// Scheduling: workgroup i runs on XCD i % 8.  All row blocks of one
-// (sequence, KV head) belong to one XCD and are numbered consecutively,
-// latest rows (longest prefixes) first, so the sequence's K/V stay in that
-// XCD's L2 while its row blocks run.  A grid of at most 256 row blocks per
-// XCD runs them longest walk first instead (ties in that order): the
-// dispatcher starts workgroups in grid order, and with two or three row
-// blocks per workgroup slot a long one that starts late sets the end of the
-// launch.
+// Scheduling: workgroup i runs on XCD i % 8, and on each XCD consecutive
+// workgroups go to its four shader engines in turn, in grid order; a
+// workgroup waits for a slot on its own shader engine, and the ones after
+// it wait too.  All row blocks of one (sequence, KV head) belong to one XCD
+// and are numbered consecutively, latest rows (longest prefixes) first, so
+// the sequence's K/V stay in that XCD's L2 while its row blocks run; each
+// window of four is rotated so that no shader engine gets the longest row
+// blocks throughout.  A grid of at most 256 row blocks per XCD runs them
+// longest walk first instead (ties in that order): with two or three row
+// blocks per workgroup slot, a long one that starts late sets the end of
+// the launch.
 //
 // 8-bit caches: the ring holds the 1-byte codes (half the bytes per stage).
 // A 16-byte K read gives 16 dims of one token, widened exactly to the
@@ -78,13 +81,16 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillNQ = 2;  // 16-row query tiles per wavefront
 constexpr int kPrefillRows = kPrefillWaves * kPrefillNQ * 16;
 constexpr int kXcds = 8;
-// Above this many row blocks per XCD the grid keeps its plain order: the
-// longest-first order costs every workgroup a select over all of its XCD's
-// row blocks (about 2 us), and with many row blocks per slot the tail it
-// saves is a small part of the launch.  Measured: 160 per XCD (13B-class
-// prefill, 8 chunks of 512 tokens x 40 heads) 99.9 -> 92.5 us, E4M3 caches
-// 98.2 -> 84.9 us; 512 per XCD (70B-class) 530 -> 550 us with the order (a
-// select over two row blocks per thread), 525 us with a precomputed order.
+// Above this many row blocks per XCD the grid keeps its plain (rotated)
+// order: the longest-first order costs every workgroup a select over all of
+// its XCD's row blocks (about 2 us), and with many row blocks per slot the
+// tail it saves is a small part of the launch.  Below it, longest first
+// also covers a long sequence that the plain order would start last.
+// Measured, 160 per XCD (13B-class prefill, 8 chunks of 512 tokens x 40
+// heads): plain order unrotated 99.9 us, rotated 89.1, longest first 90.5;
+// over E4M3 caches 98.2 / 87.5 / 84.5 us.  512 per XCD (70B-class): 530 us
+// unrotated, 550 with longest first (a select over two row blocks per
+// thread), 525 with a longest-first order precomputed on the host.
 constexpr int kPrefillOrderMaxUnits = 256;
 
 int prefill_rows_per_workgroup() { return kPrefillRows; }
@@ -207,6 +213,18 @@ prefill_mfma_kernel(PrefillArgs a) {
     // with units <= threads, item i of both passes is thread i's
     nth = counting_select<kPrefillThreads>(
         units, nth, [&](int) { return my_bucket; }, reinterpret_cast<int *>(ring));
+  }
+  if constexpr (!ORDER && !PREFIX) {
+    // The dispatcher also fixes each workgroup's shader engine: on every
+    // XCD, consecutive workgroups go to its four shader engines in turn.
+    // With a pair's row blocks consecutive and longest first, position
+    // nth % 4 would always take the same one of four neighbouring row
+    // blocks (for four row blocks per pair, always the same row block), so
+    // one shader engine would get the longest walks throughout.  Rotating
+    // each window of four positions by the window's index gives every shader
+    // engine each of the four in turn; a pair's row blocks stay together.
+    const int wi = nth >> 2;
+    if ((wi << 2) + 4 <= (int)(gridDim.x / kXcds)) nth = (wi << 2) | ((nth + wi) & 3);
   }
   const int pair = (nth / a.q_blocks) * kXcds + xcd;
   const int blk = a.q_blocks - 1 - nth % a.q_blocks;
