@@ -184,9 +184,10 @@ prefill_mfma_kernel(PrefillArgs a) {
     // super-tiles to the whole context; a long one that starts late
     // stretches the end of the launch.  Rank nth of the XCD therefore takes
     // the XCD-local row block of rank nth in an order of decreasing walk
-    // (ties in grid order, which keeps a pair's row blocks together): a
-    // counting select over the walks in super-tiles, 256 buckets of width
-    // 2^sh, one row block per thread, each walk computed as below.
+    // (ties in grid order): a counting select over the walks in super-tiles,
+    // 256 buckets of width 2^sh, one row block per thread, each walk
+    // computed as below.  Neighbouring ranks have similar walks, so the
+    // order also spreads the work evenly over the shader engines (below).
     static_assert(!PREFIX, "prefill only");
     static_assert(kPrefillOrderMaxUnits <= kPrefillThreads, "one row block per thread");
     static_assert(sizeof(ring) >= kOrderScratchInts * sizeof(int), "order scratch");
