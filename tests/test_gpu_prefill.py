@@ -332,3 +332,28 @@ def test_shared_prefix_prefill_matches_private_copies_bitwise(dtype, bs):
             max_query_len=int(w.chunk_lens().max(initial=0)))
         torch.cuda.synchronize()
         assert torch.equal(o.cpu(), out.cpu())
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 16, 4), ("f16", 8, 8)])
+def test_skewed_lengths_ordered_grid(dtype, Hq, Hkv):
+    """A small grid (at most 256 row blocks per XCD, so the longest-first
+    instantiation) with one long context among short ones: 20000 tokens
+    make the walks span more than 256 super-tiles, so the order's buckets
+    are 4 super-tiles wide, and the long sequence sits first in the batch
+    and the short ones after it.  Every output against the oracle."""
+    w = wl.build("skewed", lens=[20000, 300, 5000, 64], num_heads=Hq, num_kv_heads=Hkv,
+                 head_dim=128, block_size=16, dtype=dtype, seed=8900 + Hq,
+                 pool_factor=1.2, chunk_lens=[40, 64, 17, 64])
+    G = Hq // Hkv
+    row_blocks = -(-64 * G // 128)
+    assert 8 * -(-(w.num_seqs * Hkv) // 8) * row_blocks // 8 <= 256
+    assert w.block_tables.shape[1] * w.block_size > 256 * 32
+    print_case("prefill-skewed", w)
+    out, kc, vc = gpu_step(w)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    kh, vh = oracle_state(w)
+    want = oracle.paged_prefill(w.q, kh, vh, w.block_tables, w.context_lens,
+                                w.query_start_loc, w.scale, w.block_size,
+                                w.num_kv_heads, w.num_blocks, w.dtype)
+    compare(got, want, w.dtype, "skewed lengths, ordered grid")
